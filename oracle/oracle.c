@@ -1,0 +1,208 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU oracle for the fused-chain
+ * hot path.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the CPU
+ * baseline leg of the benchmark call it; the product path never does.  It
+ * shares no code, header or constant table with the HIP library.
+ *
+ * Everything is computed in fp64 from the exact values of the stored inputs
+ * (fp32, fp16 or bf16 bits).  No blocking, no fusion, no reordering beyond
+ * the plain definitions below.  Built with gcc -O2 -ffp-contract=off so the
+ * compiler does not fuse the fp64 multiply-adds written here.
+ *
+ * Sources (the three pages on vertical fusion):
+ *  - "C-05. Kernel Fusion 代价边界", section 3 (API / experiment form): the
+ *    stage operation y = a_s*y + b_s with ReLU on even stages; naive, fused
+ *    and fat forms all compute this same chain.
+ *  - "K4 讲解：fusion 的三笔账", section 1 (the four split plans): the chain
+ *    mm -> bias -> gelu -> residual on [M,N] outputs.
+ *  - "AIGC 基本功｜算子融合与 CUDA Graph-Fusion", section 3.5 (causal mask:
+ *    query i sees keys j <= i) and the appendix's attention-tail section (the
+ *    max / subtract / exp / sum / divide softmax steps).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------ storage decode */
+
+/* IEEE binary16 -> double, written out field by field (exact). */
+static double half_bits_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* subnormal or zero */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double: the bits are the top half of an fp32 word (exact). */
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double oracle_half_to_double(uint16_t h) { return half_bits_to_double(h); }
+double oracle_bf16_to_double(uint16_t b) { return bf16_bits_to_double(b); }
+
+/* ------------------------------------------------------------ pointwise chain */
+
+/*
+ * K-stage pointwise chain ("C-05", section 3): for s = 0 .. K-1,
+ *   y = a_s * y + b_s, then y = max(y, 0) when relu_even and s is even
+ * (stages counted from 0, the fused loop's own index).  fp64 throughout.
+ */
+void oracle_chain_f64(const float *x, double *y, int64_t n,
+                      const float *a, const float *b, int K, int relu_even)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)x[i];
+        for (int s = 0; s < K; ++s) {
+            v = (double)a[s] * v + (double)b[s];
+            if (relu_even && (s % 2) == 0 && v < 0.0)
+                v = 0.0;
+        }
+        y[i] = v;
+    }
+}
+
+/*
+ * The same chain evaluated in fp32 with exactly one rounding per stage (a
+ * correctly rounded fused multiply-add), the precision the chain's data is
+ * stored in.  fmaf() from libm is correctly rounded, so this predicts the
+ * bits of any fp32 implementation that also rounds once per stage.
+ */
+void oracle_chain_f32fma(const float *x, float *y, int64_t n,
+                         const float *a, const float *b, int K, int relu_even)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float v = x[i];
+        for (int s = 0; s < K; ++s) {
+            v = fmaf(a[s], v, b[s]);
+            if (relu_even && (s % 2) == 0 && v < 0.0f)
+                v = 0.0f;
+        }
+        y[i] = v;
+    }
+}
+
+/* ------------------------------------------------------------ GEMM + epilogue */
+
+/* GELU in its erf form: z * Phi(z) = 0.5 * z * (1 + erf(z / sqrt(2))). */
+double oracle_gelu(double z)
+{
+    return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+}
+
+/* C[i,j] = sum_k A[i,k] * B[k,j]; A [M,K], B [K,N] fp16 row-major. */
+static double dot_f16(const uint16_t *A, const uint16_t *B,
+                      int64_t N, int64_t K, int64_t i, int64_t j)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += half_bits_to_double(A[i * K + k]) * half_bits_to_double(B[k * N + j]);
+    return acc;
+}
+
+void oracle_gemm_f64(const uint16_t *A, const uint16_t *B,
+                     int64_t M, int64_t N, int64_t K, double *C)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            C[i * N + j] = dot_f16(A, B, N, K, i, j);
+}
+
+/*
+ * The four-stage chain of "K4 讲解", section 1, on one output element:
+ *   C = A.B ; C' = C + bias[j] ; C'' = GELU(C') ; Y = C'' + R[i,j].
+ */
+static double epilogue_at(const uint16_t *A, const uint16_t *B,
+                          const uint16_t *bias, const uint16_t *R,
+                          int64_t N, int64_t K, int64_t i, int64_t j)
+{
+    double c = dot_f16(A, B, N, K, i, j);
+    double c1 = c + half_bits_to_double(bias[j]);
+    double c2 = oracle_gelu(c1);
+    return c2 + half_bits_to_double(R[i * N + j]);
+}
+
+void oracle_gemm_epilogue_f64(const uint16_t *A, const uint16_t *B,
+                              const uint16_t *bias, const uint16_t *R,
+                              int64_t M, int64_t N, int64_t K, double *Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            Y[i * N + j] = epilogue_at(A, B, bias, R, N, K, i, j);
+}
+
+/* Same chain at cnt sampled (row, col) positions. */
+void oracle_gemm_epilogue_at(const uint16_t *A, const uint16_t *B,
+                             const uint16_t *bias, const uint16_t *R,
+                             int64_t M, int64_t N, int64_t K,
+                             const int64_t *rows, const int64_t *cols,
+                             int64_t cnt, double *out)
+{
+    (void)M;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < cnt; ++t)
+        out[t] = epilogue_at(A, B, bias, R, N, K, rows[t], cols[t]);
+}
+
+/* ------------------------------------------------------------ causal softmax */
+
+/*
+ * One row of the causal scaled softmax: query i of a [S,S] score block sees
+ * keys j <= i ("AIGC 基本功", section 3.5).  With z_j = scale * s_j:
+ *   m = max_{j<=i} z_j ; l = sum_{j<=i} exp(z_j - m) ;
+ *   out_j = exp(z_j - m) / l for j <= i, and exactly 0 for j > i.
+ */
+static void softmax_row(const uint16_t *srow, int64_t S, int64_t i,
+                        double scale, double *orow)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+        double z = scale * bf16_bits_to_double(srow[j]);
+        if (z > m)
+            m = z;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= i; ++j)
+        l += exp(scale * bf16_bits_to_double(srow[j]) - m);
+    for (int64_t j = 0; j < S; ++j)
+        orow[j] = (j <= i) ? exp(scale * bf16_bits_to_double(srow[j]) - m) / l : 0.0;
+}
+
+/*
+ * scores: bf16 bits [BH, S, S]; row_ids index flattened rows r = bh*S + i;
+ * out: nrows x S doubles.
+ */
+void oracle_causal_softmax_rows(const uint16_t *scores, int64_t S, double scale,
+                                const int64_t *row_ids, int64_t nrows, double *out)
+{
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < nrows; ++t) {
+        int64_t r = row_ids[t];
+        int64_t i = r % S;
+        softmax_row(scores + r * S, S, i, scale, out + t * S);
+    }
+}
+
+void oracle_causal_softmax_f64(const uint16_t *scores, int64_t BH, int64_t S,
+                               double scale, double *out)
+{
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < BH * S; ++r)
+        softmax_row(scores + r * S, S, r % S, scale, out + r * S);
+}
