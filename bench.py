@@ -1,0 +1,399 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-chain hot path on one MI355X.
+
+One step = one pass of every hot-path row over one batch of synthetic input:
+  chain    n = 16,777,216 fp32, K in {2,3,4,6,8}: naive (K launches, ping-pong)
+           and fused (1 launch); fat probe at K = 4 with 48 live fp32x4 temps
+  gemm     Y = GELU(A.B + bias) + R at M = N = K = 4096 fp16, plans
+           [1,1,1,1], [1,3], [2,2], [4]
+  softmax  causal scaled softmax over [8,16,2048,2048] bf16: fused with tile
+           64/128/256 and without skipping, plus the unfused five-step
+           baseline with its mask materialisation
+
+`value` is the fused path's HBM throughput: algorithmic bytes of the fused
+chain (all K) and the fused softmax (tile 64) divided by their summed kernel
+time.  Kernel times come from HIP events recorded on the stream the kernels are
+launched on.  HBM rows rotate over several buffer sets so repeats cannot be
+served from the 256 MiB MALL.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused-chain/softmax HBM GB/s (% peak); GEMM+epilogue TFLOP/s at 4096³ fp16"
+HBM_PEAK_GBPS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+
+CHAIN_N = 16777216
+CHAIN_KS = [2, 3, 4, 6, 8]
+CHAIN_SETS = 5                      # 5 x 128 MiB touched per rotation
+FAT_K, FAT_T = 4, 48
+GEMM_MNK = (4096, 4096, 4096)
+PLANS = [[1, 1, 1, 1], [1, 3], [2, 2], [4]]
+SM_B, SM_H, SM_S = 8, 16, 2048
+SM_TILES = [64, 128, 256, 2048]
+SCALE = 1.0 / (128.0 ** 0.5)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Event pairs on the launch stream; elapsed times collected per row."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.pending = []
+        self.ms = {}
+
+    def __call__(self, name, fn, reps=1):
+        t = self.torch
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for r in range(reps):
+            fn(r)
+        e1.record(self.stream)
+        self.pending.append((name, e0, e1, reps))
+
+    def collect(self):
+        for name, e0, e1, reps in self.pending:
+            self.ms.setdefault(name, []).append(e0.elapsed_time(e1) / reps)
+        self.pending = []
+
+    def median(self, name):
+        v = sorted(self.ms[name])
+        return v[len(v) // 2]
+
+    def minimum(self, name):
+        return min(self.ms[name])
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src):
+    """HBM traffic per launch measured with rocprofv3 counters, if the kernel
+    source is unchanged since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        tab = json.load(f)
+    row = tab.get(kernel_key)
+    if not row or row.get("source_sha") != source_hash(src):
+        return None
+    return row.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=8.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the fused chain over the K sweep on a prefix of x, and the causal softmax
+    on a slice of rows; reported in the same unit (algorithmic GB/s)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from oracle import ledger
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n = CHAIN_N
+    x, _, _ = synth.chain_inputs(n, 1)
+    t0 = time.perf_counter()
+    chain_bytes = 0
+    for K in CHAIN_KS:
+        _, a, b = synth.chain_inputs(1, K)
+        oracle.chain_f64(x, a, b, True)
+        chain_bytes += ledger.chain_bytes(n, K, True)
+    t_chain = time.perf_counter() - t0
+    # softmax: whole heads so the kept-tile accounting is exact per head
+    S = SM_S
+    s = synth.softmax_inputs(1, S, salt=11)
+    heads = 0
+    t0 = time.perf_counter()
+    t_sm = 0.0
+    rows = np.arange(S)
+    while heads < SM_B * SM_H and t_sm < budget_s:
+        oracle.causal_softmax_rows(s, SCALE, rows)
+        heads += 1
+        t_sm = time.perf_counter() - t0
+    sm_bytes = heads * ledger.softmax_bytes(1, S, 64, True)
+    total_s = t_chain + t_sm
+    gbps = (chain_bytes + sm_bytes) / total_s / 1e9
+    # GEMM + epilogue: sampled outputs of the 4096^3 chain
+    M, N, K = GEMM_MNK
+    A, B, bias, R = synth.gemm_inputs(M, N, K)
+    cnt = 65536
+    rr = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    oracle.gemm_epilogue_at(A, B, bias, R, rr.integers(0, M, cnt), rr.integers(0, N, cnt))
+    t_g = time.perf_counter() - t0
+    tflops = 2.0 * K * cnt / t_g / 1e12
+    return {
+        "value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"fp64 C oracle: fused chain K in {CHAIN_KS} on n={n} (of 16,777,216) in "
+                   f"{t_chain:.2f}s + causal softmax on {heads} [2048,2048] head(s) (of 128; one "
+                   f"synthetic head repeated) in {t_sm:.2f}s; bytes counted as the fused kernels' "
+                   f"algorithmic bytes for the same work"),
+        "gemm_epilogue": {"value": round(tflops, 6), "unit": "TFLOP/s",
+                          "sample": f"{cnt} sampled outputs of 4096^3 (2*K flops each) in {t_g:.2f}s"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", default="chain,gemm,softmax",
+                    help="comma list of row groups to run (default: all)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the hot path is single-device "
+              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_epilogues_amd as fc
+    import synth
+    from oracle import ledger  # integer ledgers only (cross-check of the accounting)
+
+    groups = set(args.rows.split(","))
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} CUs={props.multi_processor_count} gcn={getattr(props, 'gcnArchName', '?')}")
+
+    # ---------------------------------------------------------------- inputs (resident in HBM)
+    steps = []                      # callables(timer) making up one step
+    comp = {}
+
+    if "chain" in groups:
+        log("inputs: chain")
+        sets = []
+        for r in range(CHAIN_SETS):
+            x, _, _ = synth.chain_inputs(CHAIN_N, 1, salt=r)
+            xd = torch.from_numpy(x).to(dev)
+            sets.append((xd, torch.empty_like(xd), torch.empty_like(xd)))
+        coef = {K: synth.chain_inputs(1, K)[1:] for K in CHAIN_KS}
+        sink = torch.empty(fc.fc_chain_scratch_floats(CHAIN_N, FAT_K, fc.FC_CHAIN_FAT, FAT_T),
+                           dtype=torch.float32, device=dev)
+
+        def chain_rows(tm, step_i):
+            for K in CHAIN_KS:
+                a, b = coef[K]
+                tm(f"chain_fused_K{K}",
+                   lambda r, a=a, b=b: fc.fc_chain(sets[r][0], sets[r][1], a, b, True,
+                                                   fc.FC_CHAIN_FUSED), reps=CHAIN_SETS)
+                st = sets[step_i % CHAIN_SETS]
+                tm(f"chain_naive_K{K}",
+                   lambda r, a=a, b=b, st=st: fc.fc_chain(st[0], st[1], a, b, True,
+                                                          fc.FC_CHAIN_NAIVE, st[2]))
+            a, b = coef[FAT_K]
+            st = sets[(step_i + 1) % CHAIN_SETS]
+            tm(f"chain_fat_K{FAT_K}_T{FAT_T}",
+               lambda r: fc.fc_chain(st[0], st[1], a, b, True, fc.FC_CHAIN_FAT, sink, FAT_T))
+        steps.append(chain_rows)
+
+    if "gemm" in groups:
+        log("inputs: gemm 4096^3")
+        M, N, K = GEMM_MNK
+        A, B, bias, R = synth.gemm_inputs(M, N, K)
+        td = [torch.from_numpy(v.view(np.int16)).to(dev).view(torch.float16) for v in (A, B, bias, R)]
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = torch.empty(M * N, dtype=torch.float16, device=dev)
+
+        def gemm_rows(tm, step_i):
+            for plan in PLANS:
+                name = "gemm_plan" + "".join(map(str, plan))
+                tm(name, lambda r, plan=plan: fc.fc_gemm_epilogue(td[0], td[1], td[2], td[3], Y,
+                                                                  plan, ws))
+        steps.append(gemm_rows)
+
+    if "softmax" in groups:
+        log("inputs: softmax [8,16,2048,2048] bf16")
+        BH, S = SM_B * SM_H, SM_S
+        s = synth.softmax_inputs(BH, S)
+        sd = torch.from_numpy(s.view(np.int16)).to(dev).view(torch.bfloat16)
+        del s
+        out = torch.empty_like(sd)
+        wsb = fc.fc_softmax_workspace_bytes(BH, S, fc.FC_SOFTMAX_UNFUSED)
+        smws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def sm_rows(tm, step_i):
+            for tile in SM_TILES:
+                tm(f"softmax_fused_T{tile}",
+                   lambda r, tile=tile: fc.fc_causal_softmax(sd, out, SCALE, tile, fc.FC_SOFTMAX_FUSED))
+            tm("softmax_mask_materialise", lambda r: fc.fc_causal_mask_materialise(smws, BH, S))
+            tm("softmax_unfused",
+               lambda r: fc.fc_causal_softmax(sd, out, SCALE, 64, fc.FC_SOFTMAX_UNFUSED, smws))
+        steps.append(sm_rows)
+
+    # ---------------------------------------------------------------- warmup + timed region
+    tm = Timer(torch, stream)
+    log(f"warmup {args.warmup} steps")
+    for w in range(args.warmup):
+        for f in steps:
+            f(tm, w)
+    torch.cuda.synchronize()
+    tm.pending.clear()
+    tm.ms.clear()
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for f in steps:
+            f(tm, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tm.collect()
+    ms_per_step = wall / max(args.steps, 1) * 1e3
+    log(f"timed region {wall:.3f}s, {ms_per_step:.3f} ms/step")
+
+    # ---------------------------------------------------------------- derived numbers
+    fused_bytes = 0
+    fused_ms = 0.0
+    if "chain" in groups:
+        for K in CHAIN_KS:
+            bf = fc.fc_chain_bytes(CHAIN_N, K, fc.FC_CHAIN_FUSED)
+            bn = fc.fc_chain_bytes(CHAIN_N, K, fc.FC_CHAIN_NAIVE)
+            assert bf == ledger.chain_bytes(CHAIN_N, K, True) and bn == ledger.chain_bytes(CHAIN_N, K, False)
+            tf, tn = tm.median(f"chain_fused_K{K}"), tm.median(f"chain_naive_K{K}")
+            comp[f"chain_K{K}"] = {
+                "fused_us": round(tf * 1e3, 2), "naive_us": round(tn * 1e3, 2),
+                "naive_over_fused": round(tn / tf, 2),
+                "fused_GBps": round(bf / (tf * 1e-3) / 1e9, 1),
+                "fused_frac_hbm": round(bf / (tf * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "naive_GBps": round(bn / (tn * 1e-3) / 1e9, 1),
+                "launches_naive": K, "launches_fused": 1,
+                "fused_min_us": round(tm.minimum(f"chain_fused_K{K}") * 1e3, 2),
+            }
+            fused_bytes += bf
+            fused_ms += tf
+        tfat = tm.median(f"chain_fat_K{FAT_K}_T{FAT_T}")
+        comp[f"chain_fat_K{FAT_K}_T{FAT_T}"] = {
+            "us": round(tfat * 1e3, 2),
+            "fat_over_fused": round(tfat / tm.median(f"chain_fused_K{FAT_K}"), 2)}
+    if "softmax" in groups:
+        BH, S = SM_B * SM_H, SM_S
+        for tile in SM_TILES:
+            b = fc.fc_softmax_bytes(BH, S, tile, fc.FC_SOFTMAX_FUSED)
+            assert b == ledger.softmax_bytes(BH, S, tile, True)
+            t = tm.median(f"softmax_fused_T{tile}")
+            comp[f"softmax_fused_T{tile}"] = {
+                "us": round(t * 1e3, 2), "bytes": b, "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "min_us": round(tm.minimum(f"softmax_fused_T{tile}") * 1e3, 2)}
+        bu = fc.fc_softmax_bytes(BH, S, 64, fc.FC_SOFTMAX_UNFUSED)
+        tu = tm.median("softmax_unfused")
+        tmask = tm.median("softmax_mask_materialise")
+        comp["softmax_unfused"] = {"us": round(tu * 1e3, 2), "bytes": bu,
+                                   "GBps": round(bu / (tu * 1e-3) / 1e9, 1),
+                                   "mask_materialise_us": round(tmask * 1e3, 2),
+                                   "unfused_over_fused_T64": round(tu / tm.median("softmax_fused_T64"), 2)}
+        fused_bytes += fc.fc_softmax_bytes(BH, S, 64, fc.FC_SOFTMAX_FUSED)
+        fused_ms += tm.median("softmax_fused_T64")
+    if "gemm" in groups:
+        M, N, K = GEMM_MNK
+        flops = 2 * M * N * K
+        for plan in PLANS:
+            name = "gemm_plan" + "".join(map(str, plan))
+            t = tm.median(name)
+            comp[name] = {"us": round(t * 1e3, 2), "TFLOPs": round(flops / (t * 1e-3) / 1e12, 1),
+                          "frac_mfma_fp16": round(flops / (t * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+                          "bytes": fc.fc_plan_bytes(M, N, K, plan), "launches": fc.fc_plan_launches(plan),
+                          "min_us": round(tm.minimum(name) * 1e3, 2)}
+
+    value = fused_bytes / (fused_ms * 1e-3) / 1e9 if fused_ms > 0 else None
+
+    # roofline of the dominant kernel of `value`: the fused softmax at tile 64
+    roofline = None
+    if "softmax" in groups:
+        BH, S = SM_B * SM_H, SM_S
+        b = fc.fc_softmax_bytes(BH, S, 64, fc.FC_SOFTMAX_FUSED)
+        t = tm.median("softmax_fused_T64") * 1e-3
+        ach = b / t / 1e9
+        roofline = {"bound": "hbm", "kernel": "softmax_fused_kernel<4,bf16> tile 64",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "avg_launch_us": round(t * 1e6, 2), "algorithmic_bytes": b,
+                    "traffic": load_traffic("softmax_fused_T64",
+                                            os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "softmax.hip"))}
+    others = []
+    if "chain" in groups:
+        K = 8
+        b = fc.fc_chain_bytes(CHAIN_N, K, fc.FC_CHAIN_FUSED)
+        t = tm.median(f"chain_fused_K{K}") * 1e-3
+        others.append({"bound": "hbm", "kernel": "chain_fused_kernel<8,relu> n=16,777,216",
+                       "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 2),
+                       "algorithmic_bytes": b,
+                       "traffic": load_traffic("chain_fused_K8",
+                                               os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "chain.hip"))})
+    if "gemm" in groups:
+        M, N, K = GEMM_MNK
+        t = tm.median("gemm_plan4") * 1e-3
+        fl = 2 * M * N * K
+        others.append({"bound": "mfma", "kernel": "gemm_epi_kernel<256x256x64> plan [4]",
+                       "achieved": round(fl / t / 1e12, 1), "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4), "avg_launch_us": round(t * 1e6, 2),
+                       "algorithmic_flops": fl,
+                       "traffic": load_traffic("gemm_plan4",
+                                               os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "gemm.hip"))})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores)")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1) if value else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("fused pointwise chain n=16,777,216 fp32 K in {2,3,4,6,8} (naive, fused, fat K=4 T=48) "
+                         "+ causal scaled softmax [8,16,2048,2048] bf16 (fused tiles 64/128/256/none, unfused "
+                         "5-pass + mask) + GEMM+bias+GELU+residual 4096^3 fp16 plans [1,1,1,1],[1,3],[2,2],[4]"),
+            "value_definition": "algorithmic bytes of fused chain (K=2,3,4,6,8) + fused softmax (tile 64) / their summed kernel time",
+            "gemm_TFLOPs_plan4": comp.get("gemm_plan4", {}).get("TFLOPs"),
+            "device": props.name,
+        },
+        "roofline": roofline,
+        "rooflines_other": others,
+        "cpu_baseline": cpu,
+        "components": comp,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

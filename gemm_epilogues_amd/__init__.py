@@ -1,0 +1,318 @@
+"""Python binding of the fused-chain library (libfc.so, C ABI in include/fc.h).
+
+Argument marshalling only: every function here checks tensor dtypes/devices,
+passes raw device pointers and the current HIP stream to the C entry point of
+the same name, and raises FcError on a non-zero status.  All arithmetic runs
+in the HIP kernels.  Importing fails loudly when the library is not built.
+
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfc.so")
+ROOT = os.path.dirname(HERE)
+HEADER = os.path.join(ROOT, "include", "fc.h")
+
+FC_OK = 0
+FC_ERR_NULL = -1
+FC_ERR_SHAPE = -2
+FC_ERR_ALIGN = -3
+FC_ERR_PLAN = -4
+FC_ERR_UNSUPPORTED = -5
+FC_ERR_WORKSPACE = -6
+FC_ERR_HIP = -7
+FC_ERR_ALIAS = -8
+
+FC_CHAIN_NAIVE = 0
+FC_CHAIN_FUSED = 1
+FC_CHAIN_FAT = 2
+FC_SOFTMAX_FUSED = 0
+FC_SOFTMAX_UNFUSED = 1
+FC_CHAIN_MAX_STAGES = 32
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m gemm_epilogues_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+# torch ships its own HIP runtime with the same SONAME (libamdhip64.so.7) as
+# ROCm's.  Loading torch first makes libfc.so bind to that same runtime, so the
+# stream handles and device pointers torch hands out are valid in our calls.
+import torch as _torch_for_runtime  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+_RUNTIMES = _hip_runtimes_mapped()
+if len(_RUNTIMES) > 1:
+    raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(_RUNTIMES)}")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_U64 = ctypes.c_uint64
+_F = ctypes.c_float
+
+_SIGS = {
+    "fc_chain": (_I, [_P, _P, _I64, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "fc_chain_scratch_floats": (_SZ, [_I64, _I, _I, _I]),
+    "fc_gemm_epilogue": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P, _SZ, _P]),
+    "fc_gemm_workspace_bytes": (_SZ, [_I, _I, _I, _P, _I]),
+    "fc_causal_softmax": (_I, [_P, _P, _I64, _I, _F, _I, _I, _P, _SZ, _P]),
+    "fc_causal_softmax_f32out": (_I, [_P, _P, _I64, _I, _F, _I, _P]),
+    "fc_causal_softmax_tiles": (_I, [_P, _P, _P, _I64, _I, _F, _I, _P]),
+    "fc_causal_mask_materialise": (_I, [_P, _I64, _I, _P]),
+    "fc_softmax_workspace_bytes": (_SZ, [_I64, _I, _I]),
+    "fc_plan_bytes": (_U64, [_I64, _I64, _I64, _P, _I, _I]),
+    "fc_plan_launches": (_I, [_P, _I]),
+    "fc_chain_bytes": (_U64, [_I64, _I, _I]),
+    "fc_softmax_bytes": (_U64, [_I64, _I, _I, _I]),
+    "fc_status_string": (ctypes.c_char_p, [_I]),
+    "fc_version": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class FcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fc_status_string(status)} ({status})")
+
+
+def lib():
+    return _lib
+
+
+def fc_status_string(status: int) -> str:
+    return _lib.fc_status_string(int(status)).decode()
+
+
+def fc_version() -> str:
+    return _lib.fc_version().decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != FC_OK:
+        raise FcError(rc, where)
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    """Raw address of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        torch = _torch()
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _int_array(seq: Sequence[int]):
+    arr = (ctypes.c_int * max(1, len(seq)))(*[int(v) for v in seq])
+    return arr, len(seq)
+
+
+def _f32_array(seq):
+    a = np.ascontiguousarray(np.asarray(seq, dtype=np.float32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------- chain
+
+def fc_chain_scratch_floats(n: int, K: int, mode: int, fat_temps: int = 0) -> int:
+    return int(_lib.fc_chain_scratch_floats(int(n), int(K), int(mode), int(fat_temps)))
+
+
+def fc_chain(x, y, a, b, relu_even: bool = True, mode: int = FC_CHAIN_FUSED, scratch=None,
+             fat_temps: int = 0, stream=None) -> None:
+    """y = chain(x); x, y fp32 device tensors of equal size; a, b host sequences."""
+    torch = _torch()
+    _dev(x, torch.float32, "x")
+    _dev(y, torch.float32, "y")
+    _dev(scratch, torch.float32, "scratch")
+    if x.numel() != y.numel():
+        raise ValueError("x and y differ in size")
+    av, ap = _f32_array(a)
+    bv, bp = _f32_array(b)
+    if av.size != bv.size:
+        raise ValueError("a and b differ in length")
+    if scratch is not None and scratch.numel() < fc_chain_scratch_floats(x.numel(), av.size, mode, fat_temps):
+        raise ValueError("scratch too small")
+    rc = _lib.fc_chain(_ptr(x), _ptr(y), x.numel(), ap, bp, av.size, int(bool(relu_even)),
+                       int(mode), _ptr(scratch), int(fat_temps), _stream(stream))
+    _check(rc, "fc_chain")
+
+
+# ---------------------------------------------------------------- GEMM + epilogue
+
+def fc_gemm_workspace_bytes(M: int, N: int, K: int, plan: Sequence[int]) -> int:
+    arr, n = _int_array(plan)
+    return int(_lib.fc_gemm_workspace_bytes(int(M), int(N), int(K), arr, n))
+
+
+def fc_gemm_epilogue(A, B, bias, R, Y, plan: Sequence[int], workspace=None, stream=None) -> None:
+    """Y = GELU(A@B + bias) + R, fp16 device tensors A [M,K], B [K,N], bias [N], R/Y [M,N]."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (B, "B"), (bias, "bias"), (R, "R"), (Y, "Y")):
+        _dev(t, torch.float16, nm)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or bias.numel() != N or R.numel() != M * N or Y.numel() != M * N:
+        raise ValueError("shape mismatch")
+    arr, n = _int_array(plan)
+    ws_bytes = 0
+    if workspace is not None:
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.fc_gemm_epilogue(_ptr(A), _ptr(B), _ptr(bias), _ptr(R), _ptr(Y), M, N, K, arr, n,
+                               _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "fc_gemm_epilogue")
+
+
+# ---------------------------------------------------------------- causal softmax
+
+def fc_softmax_workspace_bytes(BH: int, S: int, mode: int) -> int:
+    return int(_lib.fc_softmax_workspace_bytes(int(BH), int(S), int(mode)))
+
+
+def _bhs(scores):
+    if scores.dim() == 3:
+        BH, S, S2 = scores.shape
+    elif scores.dim() == 4:
+        B, H, S, S2 = scores.shape
+        BH = B * H
+    else:
+        raise ValueError("scores must be [BH,S,S] or [B,H,S,S]")
+    if S != S2:
+        raise ValueError("scores must be square in the last two dims")
+    return BH, S
+
+
+def fc_causal_softmax(scores, out, scale: float, tile: int, mode: int = FC_SOFTMAX_FUSED,
+                      workspace=None, stream=None) -> None:
+    """out = causal softmax(scale * scores); bf16 device tensors [BH,S,S] or [B,H,S,S]."""
+    torch = _torch()
+    _dev(scores, torch.bfloat16, "scores")
+    _dev(out, torch.bfloat16, "out")
+    BH, S = _bhs(scores)
+    if out.numel() != scores.numel():
+        raise ValueError("out size mismatch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.fc_causal_softmax(_ptr(scores), _ptr(out), BH, S, float(scale), int(tile), int(mode),
+                                _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "fc_causal_softmax")
+
+
+def fc_causal_softmax_f32out(scores, out, scale: float, tile: int, stream=None) -> None:
+    torch = _torch()
+    _dev(scores, torch.bfloat16, "scores")
+    _dev(out, torch.float32, "out")
+    BH, S = _bhs(scores)
+    if out.numel() != scores.numel():
+        raise ValueError("out size mismatch")
+    rc = _lib.fc_causal_softmax_f32out(_ptr(scores), _ptr(out), BH, S, float(scale), int(tile),
+                                       _stream(stream))
+    _check(rc, "fc_causal_softmax_f32out")
+
+
+def fc_causal_softmax_tiles(scores, out, tiles_per_row, scale: float, tile: int, stream=None) -> None:
+    torch = _torch()
+    _dev(scores, torch.bfloat16, "scores")
+    _dev(out, torch.bfloat16, "out")
+    _dev(tiles_per_row, torch.int32, "tiles_per_row")
+    BH, S = _bhs(scores)
+    if tiles_per_row.numel() != BH * S:
+        raise ValueError("tiles_per_row must have BH*S entries")
+    rc = _lib.fc_causal_softmax_tiles(_ptr(scores), _ptr(out), _ptr(tiles_per_row), BH, S,
+                                      float(scale), int(tile), _stream(stream))
+    _check(rc, "fc_causal_softmax_tiles")
+
+
+def fc_causal_mask_materialise(mask, BH: int, S: int, stream=None) -> None:
+    """mask: a bf16 device tensor of >= BH*S*S elements, or a device address."""
+    if not isinstance(mask, int):
+        torch = _torch()
+        if not mask.is_cuda:
+            raise ValueError("mask must be a device tensor")
+        if mask.numel() * mask.element_size() < 2 * BH * S * S:
+            raise ValueError("mask too small")
+        if not mask.is_contiguous():
+            raise ValueError("mask must be contiguous")
+        del torch
+    rc = _lib.fc_causal_mask_materialise(_ptr(mask), int(BH), int(S), _stream(stream))
+    _check(rc, "fc_causal_mask_materialise")
+
+
+# ---------------------------------------------------------------- accounting (host only)
+
+def fc_plan_bytes(M: int, N: int, K: int, plan: Sequence[int], elem_bytes: int = 2) -> int:
+    arr, n = _int_array(plan)
+    return int(_lib.fc_plan_bytes(int(M), int(N), int(K), arr, n, int(elem_bytes)))
+
+
+def fc_plan_launches(plan: Sequence[int]) -> int:
+    arr, n = _int_array(plan)
+    return int(_lib.fc_plan_launches(arr, n))
+
+
+def fc_chain_bytes(n: int, K: int, mode: int) -> int:
+    return int(_lib.fc_chain_bytes(int(n), int(K), int(mode)))
+
+
+def fc_softmax_bytes(BH: int, S: int, tile: int, mode: int) -> int:
+    return int(_lib.fc_softmax_bytes(int(BH), int(S), int(tile), int(mode)))

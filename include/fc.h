@@ -1,0 +1,195 @@
+/*
+ * fc.h -- C ABI of the fused-chain library for AMD Instinct MI355X (gfx950).
+ *
+ * Vertical fusion of three operator chains: intermediates stay in VGPRs or
+ * LDS instead of making HBM round trips.
+ *
+ * Conventions for every entry point:
+ *  - Plain C types only; no exceptions cross the boundary.
+ *  - The caller owns all memory.  Device pointers must point to device memory
+ *    of the current HIP device; "host" pointers to ordinary host memory.
+ *  - The library never allocates, frees or synchronises.  Compute entry points
+ *    validate their arguments synchronously, before any HIP call, then enqueue
+ *    kernels on `stream` (NULL = the null stream) and return.
+ *  - Layouts are row-major and contiguous.
+ *  - Return value: FC_OK or one of the negative FC_ERR_* codes.  On any
+ *    validation error nothing is enqueued.  FC_ERR_HIP means a launch failed
+ *    (hipGetLastError after the launch); the stream state is then undefined.
+ *  - The library keeps no state; every entry point is re-entrant.
+ */
+#ifndef FC_H
+#define FC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *fc_stream;   /* the same type as hipStream_t */
+
+enum {
+    FC_OK = 0,
+    FC_ERR_NULL = -1,         /* a required pointer is NULL                      */
+    FC_ERR_SHAPE = -2,        /* a size is negative or zero where not allowed     */
+    FC_ERR_ALIGN = -3,        /* a pointer is not 16-byte aligned                 */
+    FC_ERR_PLAN = -4,         /* split plan is not a composition of 4             */
+    FC_ERR_UNSUPPORTED = -5,  /* valid but unsupported (K stages, tile, temps...) */
+    FC_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required       */
+    FC_ERR_HIP = -7,          /* a HIP launch failed                              */
+    FC_ERR_ALIAS = -8         /* buffers overlap where they must not              */
+};
+
+enum { FC_CHAIN_NAIVE = 0, FC_CHAIN_FUSED = 1, FC_CHAIN_FAT = 2 };
+enum { FC_SOFTMAX_FUSED = 0, FC_SOFTMAX_UNFUSED = 1 };
+
+#define FC_CHAIN_MAX_STAGES 32
+
+/* ------------------------------------------------------------------ chain */
+
+/*
+ * fc_chain -- K-stage pointwise chain ("C-05. Kernel Fusion 代价边界", section 3,
+ * the API / experiment-form table and the stage operation under it):
+ *     for s = 0 .. K-1:  y = a[s] * y + b[s];  if (relu_even && s % 2 == 0) y = max(y, 0)
+ * Every stage is one fused multiply-add (a single rounding) in fp32, so the
+ * three modes produce bit-identical y.
+ *
+ *  x        device, fp32 [n], 16-byte aligned.  May equal y (in place); any
+ *           other overlap with y is undefined.
+ *  y        device, fp32 [n], 16-byte aligned.
+ *  n        number of elements, n >= 0 (n == 0 enqueues nothing).
+ *  a, b     HOST arrays of K fp32 coefficients, copied into the launch.
+ *  K        1 .. FC_CHAIN_MAX_STAGES.
+ *  mode     FC_CHAIN_NAIVE: K launches, stage s reads the previous stage's
+ *                 buffer and writes the other (ping-pong between y and
+ *                 scratch, the last stage lands in y);
+ *           FC_CHAIN_FUSED: one launch, all K stages in registers;
+ *           FC_CHAIN_FAT:   FUSED plus `fat_temps` live fp32x4 temporaries per
+ *                 lane, reduced into a sink so they cannot be eliminated (a
+ *                 register-pressure probe, not a production form).
+ *  scratch  device, fp32; NAIVE with K >= 2: n floats, 16-byte aligned, must
+ *           not overlap x or y.  FAT: the sink, fc_chain_scratch_floats()
+ *           floats.  FUSED: ignored (may be NULL).
+ *  fat_temps  FAT only: one of 0, 16, 48, 96, 128; FAT supports K in {1,2,3,4,6,8}.
+ */
+int fc_chain(const float *x, float *y, int64_t n, const float *a, const float *b, int K,
+             int relu_even, int mode, float *scratch, int fat_temps, fc_stream stream);
+
+/* Floats of scratch fc_chain needs for (n, K, mode, fat_temps); 0 if none. */
+size_t fc_chain_scratch_floats(int64_t n, int K, int mode, int fat_temps);
+
+/* -------------------------------------------------------- GEMM + epilogue */
+
+/*
+ * fc_gemm_epilogue -- Y = GELU(A.B + bias) + R, the four-operator chain
+ * mm -> bias -> gelu -> res of "K4 讲解：fusion 的三笔账", section 1, cut into
+ * kernels by a split plan.  GELU is the erf form 0.5*z*(1 + erf(z/sqrt(2))).
+ *
+ *  A     device fp16 [M,K];  B device fp16 [K,N];  bias device fp16 [N];
+ *  R     device fp16 [M,N];  Y device fp16 [M,N] (must not overlap A, B,
+ *        bias or R).  All 16-byte aligned.
+ *  M >= 1; N >= 8 and K >= 8, both multiples of 8.
+ *  plan  HOST array of plan_len positive segment lengths summing to 4, e.g.
+ *        {1,1,1,1}, {1,3}, {2,2}, {4}; all 8 compositions are accepted.  Each
+ *        segment is one kernel: the first is the MFMA GEMM with the
+ *        segment's operators applied on the accumulator registers; later
+ *        segments are pointwise kernels.  At every cut the running value is
+ *        rounded to fp16 and written to the workspace, and the next kernel
+ *        reads it back.  Arithmetic is fp32 between cuts; Y is rounded to fp16
+ *        (round to nearest even).
+ *  workspace  device, >= fc_gemm_workspace_bytes() bytes, 16-byte aligned
+ *        (NULL allowed when that is 0).  After a plan whose first segment is
+ *        the bare GEMM, the workspace holds C = A.B as fp16 until the next
+ *        segment overwrites it in place.
+ */
+int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                     const uint16_t *R, uint16_t *Y, int M, int N, int K,
+                     const int *plan, int plan_len, void *workspace, size_t ws_bytes,
+                     fc_stream stream);
+
+/* Bytes of workspace for a plan: 2*M*N when the plan has a cut, else 0;
+ * 0 also for an invalid plan (fc_gemm_epilogue then returns FC_ERR_PLAN). */
+size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_len);
+
+/* ---------------------------------------------------- causal softmax */
+
+/*
+ * fc_causal_softmax -- causal scaled-masked softmax over attention scores
+ * ("AIGC 基本功｜算子融合与 CUDA Graph-Fusion", section 3.5, causal mask and
+ * block skipping; appendix attention-tail section, the five steps).  For
+ * every row (bh, i) with z_j = scale * scores[bh, i, j]:
+ *     out[bh, i, j] = exp(z_j - max_{k<=i} z_k) / sum_{k<=i} exp(z_k - max) for j <= i,
+ *     out[bh, i, j] = 0 exactly for j > i.
+ *
+ *  scores  device bf16 [BH, S, S];  out device bf16 [BH, S, S] (round to
+ *          nearest even; must not overlap scores).  16-byte aligned.
+ *  BH >= 1, S >= 1.
+ *  tile    FUSED: key-tile edge for block skipping, 64, 128, 256, or S (no
+ *          skipping).  Row i loads only key tiles 0 .. floor(i/tile); the rest
+ *          of the row is written as zeros without being read.  UNFUSED: ignored.
+ *  mode    FC_SOFTMAX_FUSED: one kernel, one pass over the kept tiles.
+ *          FC_SOFTMAX_UNFUSED: the five-step baseline -- row max of scale*s over
+ *          the whole row; x = scale*s - max; e = exp(x) * mask; row sum; e/sum
+ *          -- each step its own kernel, bf16 intermediates in `out`, fp32 row
+ *          statistics, and a materialised bf16 0/1 mask.
+ *  workspace  UNFUSED: device, >= fc_softmax_workspace_bytes() bytes, laid out
+ *          as [mask bf16 BH*S*S, padded to a multiple of 256 bytes]
+ *          [row max fp32 BH*S][row sum fp32 BH*S]; the
+ *          mask part must have been filled by fc_causal_mask_materialise()
+ *          for the same (BH, S).  FUSED: ignored (may be NULL).
+ */
+int fc_causal_softmax(const uint16_t *scores, uint16_t *out, int64_t BH, int S, float scale,
+                      int tile, int mode, void *workspace, size_t ws_bytes, fc_stream stream);
+
+/* The fused kernel with fp32 output (same arithmetic; only the store type
+ * differs).  out: device fp32 [BH, S, S], 16-byte aligned. */
+int fc_causal_softmax_f32out(const uint16_t *scores, float *out, int64_t BH, int S, float scale,
+                             int tile, fc_stream stream);
+
+/* The fused kernel, also writing for every row the number of key tiles it
+ * loaded (device int32 [BH*S]).  For checking block skipping. */
+int fc_causal_softmax_tiles(const uint16_t *scores, uint16_t *out, int32_t *tiles_per_row,
+                            int64_t BH, int S, float scale, int tile, fc_stream stream);
+
+/* Writes the causal mask as bf16 1.0 (key j <= query i) / 0.0 (j > i) into
+ * mask [BH, S, S] (device, 16-byte aligned). */
+int fc_causal_mask_materialise(uint16_t *mask, int64_t BH, int S, fc_stream stream);
+
+/* UNFUSED: round_up(2*BH*S*S, 256) + 8*BH*S bytes; FUSED: 0. */
+size_t fc_softmax_workspace_bytes(int64_t BH, int S, int mode);
+
+/* ------------------------------------------------------------ accounting */
+
+/*
+ * Algorithmic DRAM bytes and launches, pure host integer functions (no device).
+ *
+ * fc_plan_bytes: bytes of a split plan of the GEMM epilogue chain ("K4 讲解",
+ *   section 1): every external operand (A, B, bias, R) is read once, Y written
+ *   once, and every cut writes one [M,N] intermediate and reads it back:
+ *     elem_bytes * (M*K + K*N + N + 2*M*N + 2*cuts*M*N);  0 for an invalid plan.
+ * fc_plan_launches: number of segments; 0 for an invalid plan.
+ * fc_chain_bytes: fp32 chain, NAIVE 8*K*n, FUSED and FAT 8*n (the fat sink is
+ *   probe overhead and not counted) ("AIGC 基本功", section 3.2).
+ * fc_softmax_bytes: FUSED reads each row's kept tiles and writes the whole
+ *   output: 2*(BH*sum_i min(S, (floor(i/tile)+1)*tile) + BH*S*S);
+ *   UNFUSED 2*BH*S*S*(8 + 1 mask) + 16*BH*S (fp32 row statistics written and
+ *   read once each).  0 for invalid arguments.
+ */
+uint64_t fc_plan_bytes(int64_t M, int64_t N, int64_t K, const int *plan, int plan_len,
+                       int elem_bytes);
+int fc_plan_launches(const int *plan, int plan_len);
+uint64_t fc_chain_bytes(int64_t n, int K, int mode);
+uint64_t fc_softmax_bytes(int64_t BH, int S, int tile, int mode);
+
+/* Static text for a status code. */
+const char *fc_status_string(int status);
+
+/* Library version string. */
+const char *fc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FC_H */

@@ -1,0 +1,181 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, its integer accounting equals the oracle's stage-walking
+ledgers (and the values the pages print), and invalid arguments are rejected
+before any HIP call.
+
+Every validation case below is invalid by construction, so no kernel is ever
+launched from this file (the pointers are fake host addresses).
+"""
+import ctypes
+import re
+
+import pytest
+
+import gemm_epilogues_amd as fc
+from oracle import ledger
+from conftest import load_golden
+
+FAKE = 0x10000          # a 16-byte aligned address that is never dereferenced
+MIS = 0x10004           # misaligned
+
+
+def declared_symbols():
+    text = open(fc.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(fc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fc.EXPORTED)
+    assert "gfx950" in fc.fc_version()
+
+
+def test_status_strings():
+    for code in range(0, -9, -1):
+        assert fc.fc_status_string(code) != "unknown status"
+    assert fc.fc_status_string(-99) == "unknown status"
+
+
+def test_plan_accounting_matches_ledger_and_page():
+    g = load_golden("k4_split_plans.json")
+    for row in g["plans"]:
+        assert fc.fc_plan_bytes(4096, 4096, 4096, row["plan"]) == row["bytes"]
+        assert fc.fc_plan_launches(row["plan"]) == row["launches"]
+    for M, N, K in [(16, 4096, 4096), (1, 8, 8), (17, 40, 24), (4096, 4096, 4096), (300, 1000, 72)]:
+        for plan in ledger.compositions(4):
+            assert fc.fc_plan_bytes(M, N, K, plan) == ledger.plan_bytes(M, N, K, plan)
+            assert fc.fc_plan_bytes(M, N, K, plan, 4) == ledger.plan_bytes(M, N, K, plan, 4)
+            assert fc.fc_plan_launches(plan) == ledger.plan_launches(plan) == len(plan)
+            ws = fc.fc_gemm_workspace_bytes(M, N, K, plan)
+            assert ws == (2 * M * N if len(plan) > 1 else 0)
+
+
+@pytest.mark.parametrize("plan", [[], [0, 4], [5], [1, 1, 1], [2, -1, 3], [1, 1, 1, 1, 0]])
+def test_bad_plan_accounting_is_zero(plan):
+    assert fc.fc_plan_bytes(16, 16, 16, plan) == 0
+    assert fc.fc_plan_launches(plan) == 0
+    assert fc.fc_gemm_workspace_bytes(16, 16, 16, plan) == 0
+
+
+def test_chain_accounting_matches_ledger():
+    for n in (0, 1, 5, 1048576, 16777216):
+        for K in (1, 2, 3, 4, 6, 8, 32):
+            assert fc.fc_chain_bytes(n, K, fc.FC_CHAIN_NAIVE) == ledger.chain_bytes(n, K, False)
+            assert fc.fc_chain_bytes(n, K, fc.FC_CHAIN_FUSED) == ledger.chain_bytes(n, K, True)
+            assert fc.fc_chain_bytes(n, K, fc.FC_CHAIN_FAT) == ledger.chain_bytes(n, K, True)
+            assert fc.fc_chain_bytes(n, K, fc.FC_CHAIN_NAIVE) == K * fc.fc_chain_bytes(n, K, fc.FC_CHAIN_FUSED)
+
+
+def test_softmax_accounting_matches_ledger():
+    for BH, S in [(1, 1), (2, 3), (3, 63), (1, 64), (2, 65), (1, 129), (4, 300), (128, 2048)]:
+        for tile in (64, 128, 256, S):
+            assert fc.fc_softmax_bytes(BH, S, tile, fc.FC_SOFTMAX_FUSED) == \
+                ledger.softmax_bytes(BH, S, tile, True), (BH, S, tile)
+        assert fc.fc_softmax_bytes(BH, S, 64, fc.FC_SOFTMAX_UNFUSED) == ledger.softmax_bytes(BH, S, 64, False)
+    assert fc.fc_softmax_bytes(128, 2048, 64, fc.FC_SOFTMAX_FUSED) == 1627389952
+    assert fc.fc_softmax_bytes(128, 2048, 2048, fc.FC_SOFTMAX_FUSED) == 2 * 1024 ** 3
+    assert fc.fc_softmax_bytes(128, 2048, 32, fc.FC_SOFTMAX_FUSED) == 0
+
+
+def test_workspace_sizes():
+    assert fc.fc_softmax_workspace_bytes(128, 2048, fc.FC_SOFTMAX_FUSED) == 0
+    assert fc.fc_softmax_workspace_bytes(128, 2048, fc.FC_SOFTMAX_UNFUSED) == 2 * 128 * 2048 ** 2 + 8 * 128 * 2048
+    assert fc.fc_softmax_workspace_bytes(1, 3, fc.FC_SOFTMAX_UNFUSED) == 256 + 8 * 3
+    assert fc.fc_chain_scratch_floats(1000, 4, fc.FC_CHAIN_NAIVE) == 1000
+    assert fc.fc_chain_scratch_floats(1000, 1, fc.FC_CHAIN_NAIVE) == 0
+    assert fc.fc_chain_scratch_floats(1000, 4, fc.FC_CHAIN_FUSED) == 0
+    assert fc.fc_chain_scratch_floats(1 << 24, 4, fc.FC_CHAIN_FAT, 48) == 2048 * 256 * 4
+
+
+# ---------------------------------------------------------------- validation (no HIP call)
+
+def _f32(vals):
+    import numpy as np
+    a = np.asarray(vals, dtype=np.float32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+L = fc.lib()
+
+
+def test_chain_validation():
+    a, ap = _f32([1.0, 2.0])
+    b, bp = _f32([0.0, 0.0])
+    # negative n
+    assert L.fc_chain(FAKE, FAKE, -1, ap, bp, 2, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_SHAPE
+    # K out of range
+    assert L.fc_chain(FAKE, FAKE, 8, ap, bp, 0, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_chain(FAKE, FAKE, 8, ap, bp, 33, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    # bad mode
+    assert L.fc_chain(FAKE, FAKE, 8, ap, bp, 2, 1, 7, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    # null coefficients / data
+    assert L.fc_chain(FAKE, FAKE, 8, None, bp, 2, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_NULL
+    assert L.fc_chain(None, FAKE, 8, ap, bp, 2, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_NULL
+    # misaligned
+    assert L.fc_chain(MIS, FAKE + 4096, 8, ap, bp, 2, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_ALIGN
+    # partial overlap of x and y
+    assert L.fc_chain(FAKE, FAKE + 16, 8, ap, bp, 2, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_ERR_ALIAS
+    # naive without scratch / misaligned scratch / overlapping scratch
+    assert L.fc_chain(FAKE, FAKE + 4096, 8, ap, bp, 2, 1, fc.FC_CHAIN_NAIVE, None, 0, None) == fc.FC_ERR_WORKSPACE
+    assert L.fc_chain(FAKE, FAKE + 4096, 8, ap, bp, 2, 1, fc.FC_CHAIN_NAIVE, MIS + 8192, 0, None) == fc.FC_ERR_ALIGN
+    assert L.fc_chain(FAKE, FAKE + 4096, 8, ap, bp, 2, 1, fc.FC_CHAIN_NAIVE, FAKE + 16, 0, None) == fc.FC_ERR_ALIAS
+    # fat: unsupported temps / stages
+    assert L.fc_chain(FAKE, FAKE + 4096, 8, ap, bp, 2, 1, fc.FC_CHAIN_FAT, FAKE + 8192, 7, None) == fc.FC_ERR_UNSUPPORTED
+    a5, ap5 = _f32([1.0] * 5)
+    assert L.fc_chain(FAKE, FAKE + 4096, 8, ap5, ap5, 5, 1, fc.FC_CHAIN_FAT, FAKE + 8192, 48, None) == fc.FC_ERR_UNSUPPORTED
+    a2, _ = a, b
+    assert L.fc_chain(FAKE, FAKE + 4096, 8, ap, bp, 2, 1, fc.FC_CHAIN_FAT, FAKE + 8192, 96, None) == fc.FC_ERR_UNSUPPORTED
+    # n == 0 is a no-op that enqueues nothing
+    assert L.fc_chain(None, None, 0, ap, bp, 2, 1, fc.FC_CHAIN_FUSED, None, 0, None) == fc.FC_OK
+
+
+def _plan(p):
+    arr = (ctypes.c_int * max(1, len(p)))(*p)
+    return arr, len(p)
+
+
+def test_gemm_validation():
+    p4, n4 = _plan([4])
+    p13, n13 = _plan([1, 3])
+    A, B, bias, R, Y = FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20), FAKE + (4 << 20)
+    W = FAKE + (5 << 20)
+    for bad in ([0, 4], [5], [1, 1, 1], [], [1, 1, 1, 1, 0]):
+        pb, nb = _plan(bad)
+        assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 64, pb, nb, W, 1 << 20, None) == fc.FC_ERR_PLAN
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 64, None, 1, W, 1 << 20, None) == fc.FC_ERR_PLAN
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 0, 64, 64, p4, n4, None, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 60, 64, p4, n4, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 12, p4, n4, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_gemm_epilogue(A, B, None, R, Y, 16, 64, 64, p4, n4, None, 0, None) == fc.FC_ERR_NULL
+    assert L.fc_gemm_epilogue(A, B, bias, R, MIS, 16, 64, 64, p4, n4, None, 0, None) == fc.FC_ERR_ALIGN
+    assert L.fc_gemm_epilogue(A, B, bias, R, R, 16, 64, 64, p4, n4, None, 0, None) == fc.FC_ERR_ALIAS
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 64, p13, n13, None, 0, None) == fc.FC_ERR_WORKSPACE
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 64, p13, n13, W, 16 * 64 * 2 - 2, None) == fc.FC_ERR_WORKSPACE
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 64, p13, n13, MIS + (6 << 20), 1 << 20, None) == fc.FC_ERR_ALIGN
+    assert L.fc_gemm_epilogue(A, B, bias, R, Y, 16, 64, 64, p13, n13, Y, 1 << 20, None) == fc.FC_ERR_ALIAS
+
+
+def test_softmax_validation():
+    s, o, w = FAKE, FAKE + (1 << 24), FAKE + (2 << 24)
+    assert L.fc_causal_softmax(s, o, 0, 64, 0.1, 64, fc.FC_SOFTMAX_FUSED, None, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fc_causal_softmax(s, o, 1, 0, 0.1, 64, fc.FC_SOFTMAX_FUSED, None, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fc_causal_softmax(None, o, 1, 64, 0.1, 64, fc.FC_SOFTMAX_FUSED, None, 0, None) == fc.FC_ERR_NULL
+    assert L.fc_causal_softmax(MIS, o, 1, 64, 0.1, 64, fc.FC_SOFTMAX_FUSED, None, 0, None) == fc.FC_ERR_ALIGN
+    assert L.fc_causal_softmax(s, s + 32, 1, 64, 0.1, 64, fc.FC_SOFTMAX_FUSED, None, 0, None) == fc.FC_ERR_ALIAS
+    for tile in (0, 32, 100, 512):
+        assert L.fc_causal_softmax(s, o, 1, 1024, 0.1, tile, fc.FC_SOFTMAX_FUSED, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_causal_softmax(s, o, 1, 64, 0.1, 64, 5, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    need = fc.fc_softmax_workspace_bytes(1, 64, fc.FC_SOFTMAX_UNFUSED)
+    assert L.fc_causal_softmax(s, o, 1, 64, 0.1, 64, fc.FC_SOFTMAX_UNFUSED, None, 0, None) == fc.FC_ERR_WORKSPACE
+    assert L.fc_causal_softmax(s, o, 1, 64, 0.1, 64, fc.FC_SOFTMAX_UNFUSED, w, need - 1, None) == fc.FC_ERR_WORKSPACE
+    assert L.fc_causal_softmax(s, o, 1, 64, 0.1, 64, fc.FC_SOFTMAX_UNFUSED, o, need, None) == fc.FC_ERR_ALIAS
+    assert L.fc_causal_softmax_f32out(s, o, 1, 64, 0.1, 48, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_causal_softmax_tiles(s, o, None, 1, 64, 0.1, 64, None) == fc.FC_ERR_NULL
+    assert L.fc_causal_mask_materialise(None, 1, 4, None) == fc.FC_ERR_NULL
+    assert L.fc_causal_mask_materialise(MIS, 1, 4, None) == fc.FC_ERR_ALIGN
+    assert L.fc_causal_mask_materialise(FAKE, 0, 4, None) == fc.FC_ERR_SHAPE

@@ -1,0 +1,131 @@
+"""GPU parity of the fp16 GEMM + bias + erf-GELU + residual chain for every
+split plan ("K4 讲解：fusion 的三笔账", section 1) against the fp64 oracle.
+
+Bar: |Y - ref| <= 1e-2 * (1 + |ref|) elementwise for every plan; the GEMM
+alone is bit-exact on integer-valued inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import ledger
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_epilogues_amd as fc  # noqa: E402
+from gpu_util import f16_from_bits, bits, announce  # noqa: E402
+
+ALL_PLANS = ledger.compositions(4)
+NAMED_PLANS = [[1, 1, 1, 1], [1, 3], [2, 2], [4]]
+
+
+def tol_ok(y_bits, ref):
+    y = y_bits.view(np.float16).astype(np.float64)
+    err = np.abs(y - ref)
+    bound = 1e-2 * (1.0 + np.abs(ref))
+    return bool(np.all(err <= bound)), float(np.max(err / bound))
+
+
+class Dev:
+    def __init__(self, M, N, K, salt=0, int_valued=False):
+        self.M, self.N, self.K = M, N, K
+        if int_valued:
+            A, B = synth.gemm_int_inputs(M, N, K, salt)
+            _, _, bias, R = synth.gemm_inputs(M, N, K, salt)
+        else:
+            A, B, bias, R = synth.gemm_inputs(M, N, K, salt)
+        self.h = (A, B, bias, R)
+        self.A, self.B, self.bias, self.R = (f16_from_bits(t) for t in self.h)
+
+    def run(self, plan, keep_ws=False):
+        Y = torch.empty((self.M, self.N), dtype=torch.float16, device="cuda")
+        wsb = fc.fc_gemm_workspace_bytes(self.M, self.N, self.K, plan)
+        ws = torch.empty(max(wsb // 2, 1), dtype=torch.float16, device="cuda") if wsb else None
+        fc.fc_gemm_epilogue(self.A, self.B, self.bias, self.R, Y, plan, ws)
+        torch.cuda.synchronize()
+        if keep_ws:
+            return bits(Y), (bits(ws)[: self.M * self.N].reshape(self.M, self.N) if ws is not None else None)
+        return bits(Y)
+
+
+SMALL = [(1, 8, 8), (3, 16, 40), (16, 64, 64), (17, 40, 24), (33, 72, 136), (64, 128, 256),
+         (100, 264, 520), (129, 136, 72), (256, 256, 64), (300, 520, 1000)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_all_plans_small_shapes(M, N, K):
+    announce(f"gemm M={M} N={N} K={K} all plans")
+    d = Dev(M, N, K, salt=M + N + K)
+    ref = oracle.gemm_epilogue_f64(*d.h)
+    for plan in ALL_PLANS:
+        ok, worst = tol_ok(d.run(plan), ref)
+        assert ok, (plan, worst)
+
+
+def test_big_tile_path_all_plans():
+    """Shapes that take the 256x256 tile kernel (>= 128 tiles), with ragged M."""
+    M, N, K = 2048 + 37, 4096, 264
+    announce(f"gemm big tiles M={M} N={N} K={K}")
+    d = Dev(M, N, K, salt=5)
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([rng.integers(0, M, 3000), [0, M - 1, 255, 256, 2047, 2048]])
+    cols = np.concatenate([rng.integers(0, N, 3000), [0, N - 1, 255, 256, 31, 32]])
+    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
+    for plan in ALL_PLANS:
+        Y = d.run(plan)
+        ok, worst = tol_ok(Y[rows, cols], ref)
+        assert ok, (plan, worst)
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 256, 4096])
+def test_integer_gemm_exact_in_workspace(M):
+    """A, B in {-1,0,1}: plan [1,3] leaves C = A.B (fp16) in the workspace,
+    bit-exact against the integer product."""
+    N, K = (4096, 1024) if M == 4096 else (2048, 2048)
+    announce(f"gemm integer exact M={M} N={N} K={K}")
+    d = Dev(M, N, K, salt=M, int_valued=True)
+    _, C = d.run([1, 3], keep_ws=True)
+    A = d.h[0].view(np.float16).astype(np.float64)
+    B = d.h[1].view(np.float16).astype(np.float64)
+    exact = A @ B            # integer sums of magnitude <= K: exact in fp64
+    assert np.array_equal(C.view(np.float16).astype(np.float64), exact)
+
+
+def test_decode_config_all_plans():
+    """M = 16, N = K = 4096 (decode shape), every plan against the full oracle."""
+    announce("gemm decode 16x4096x4096")
+    d = Dev(16, 4096, 4096)
+    ref = oracle.gemm_epilogue_f64(*d.h)
+    outs = {}
+    for plan in ALL_PLANS:
+        Y = d.run(plan)
+        ok, worst = tol_ok(Y, ref)
+        assert ok, (plan, worst)
+        outs[tuple(plan)] = Y
+    # the fused plan's only rounding is the final one
+    y4 = outs[(4,)].view(np.float16).astype(np.float64)
+    assert np.max(np.abs(y4 - ref) / (1 + np.abs(ref))) <= 2.0 ** -10
+
+
+def test_square_4096_config_sampled():
+    """M = N = K = 4096: sampled outputs (incl. tile corners) against the oracle."""
+    announce("gemm 4096^3 sampled")
+    d = Dev(4096, 4096, 4096)
+    rng = np.random.default_rng(2)
+    rows = np.concatenate([rng.integers(0, 4096, 4000), [0, 4095, 255, 256, 4095, 0]])
+    cols = np.concatenate([rng.integers(0, 4096, 4000), [0, 4095, 256, 255, 0, 4095]])
+    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
+    ys = {}
+    for plan in NAMED_PLANS:
+        Y = d.run(plan)
+        ok, worst = tol_ok(Y[rows, cols], ref)
+        assert ok, (plan, worst)
+        ys[tuple(plan)] = Y.view(np.float16).astype(np.float32)
+    # plans differ only by fp16 rounding at the cuts
+    for p, y in ys.items():
+        assert np.max(np.abs(y - ys[(4,)]) / (1 + np.abs(ys[(4,)]))) <= 1e-2, p

@@ -1,0 +1,184 @@
+"""GPU parity of the causal scaled-masked softmax (fused with block skipping,
+and the unfused five-step baseline) against the fp64 oracle.  Definition:
+"AIGC 基本功｜算子融合与 CUDA Graph-Fusion", section 3.5 and the appendix's
+attention-tail section.
+
+Bar: |out - ref| <= 1e-2 absolute; the causal zero pattern exact; rows of the
+fp32-output mode sum to 1 within 1e-3; bf16 rows within 1e-3 plus half an
+ulp per stored entry; tiles visited per row exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_epilogues_amd as fc  # noqa: E402
+from gpu_util import bf16_from_bits, bits, announce  # noqa: E402
+
+SCALE = float(np.float32(1.0 / np.sqrt(128.0)))
+
+
+def bf16_vals(u16):
+    return synth.bf16_bits_to_f32(u16).astype(np.float64)
+
+
+def bf16_half_ulp(v):
+    """Half an ulp of bf16 at each (non-negative) value."""
+    v = np.maximum(np.abs(v), 2.0 ** -126)
+    e = np.floor(np.log2(v))
+    return 0.5 * 2.0 ** (e - 7)
+
+
+def check_against_ref(out_bits, ref, S):
+    out = bf16_vals(out_bits)
+    assert np.max(np.abs(out - ref)) <= 1e-2
+    iu = np.triu_indices(S, 1)
+    il = np.tril_indices(S)
+    o3 = out.reshape(-1, S, S)
+    assert np.all(o3[:, iu[0], iu[1]] == 0.0)
+    assert np.all(o3[:, il[0], il[1]] > 0.0)
+    sums = o3.sum(axis=2)
+    slack = 1e-3 + bf16_half_ulp(o3).sum(axis=2)
+    assert np.all(np.abs(sums - 1.0) <= slack)
+
+
+def run_fused(s_dev, BH, S, tile, f32=False):
+    if f32:
+        out = torch.empty((BH, S, S), dtype=torch.float32, device="cuda")
+        fc.fc_causal_softmax_f32out(s_dev, out, SCALE, tile)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+    out = torch.empty((BH, S, S), dtype=torch.bfloat16, device="cuda")
+    fc.fc_causal_softmax(s_dev, out, SCALE, tile, fc.FC_SOFTMAX_FUSED)
+    torch.cuda.synchronize()
+    return bits(out)
+
+
+def run_unfused(s_dev, BH, S):
+    out = torch.empty((BH, S, S), dtype=torch.bfloat16, device="cuda")
+    wsb = fc.fc_softmax_workspace_bytes(BH, S, fc.FC_SOFTMAX_UNFUSED)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    fc.fc_causal_mask_materialise(ws, BH, S)
+    fc.fc_causal_softmax(s_dev, out, SCALE, 64, fc.FC_SOFTMAX_UNFUSED, ws)
+    torch.cuda.synchronize()
+    mask = ws[: 2 * BH * S * S].view(torch.int16).cpu().numpy().view(np.uint16).reshape(BH, S, S)
+    return bits(out), mask
+
+
+SHAPES = [(1, 1), (2, 2), (1, 3), (2, 63), (1, 64), (2, 65), (1, 129), (3, 256), (1, 640), (2, 1000),
+          (1, 1024), (2, 2048)]
+
+
+@pytest.mark.parametrize("BH,S", SHAPES)
+def test_fused_every_tile(BH, S):
+    announce(f"softmax fused BH={BH} S={S}")
+    s = synth.softmax_inputs(BH, S, salt=S)
+    ref = oracle.causal_softmax_f64(s, SCALE)
+    sd = bf16_from_bits(s)
+    for tile in (64, 128, 256, S):
+        check_against_ref(run_fused(sd, BH, S, tile), ref, S)
+
+
+@pytest.mark.parametrize("BH,S", [(1, 1), (2, 65), (1, 640), (2, 2048)])
+def test_fused_f32_rows_sum_to_one(BH, S):
+    announce(f"softmax fused f32out BH={BH} S={S}")
+    s = synth.softmax_inputs(BH, S, salt=S + 1)
+    ref = oracle.causal_softmax_f64(s, SCALE)
+    out = run_fused(bf16_from_bits(s), BH, S, 64, f32=True).astype(np.float64)
+    assert np.max(np.abs(out - ref)) <= 1e-4
+    assert np.all(np.abs(out.sum(axis=2) - 1.0) <= 1e-3)
+
+
+@pytest.mark.parametrize("BH,S", [(1, 3), (2, 65), (1, 640), (1, 2048)])
+def test_tiles_visited_exact(BH, S):
+    announce(f"softmax tiles BH={BH} S={S}")
+    s = synth.softmax_inputs(BH, S, salt=3)
+    sd = bf16_from_bits(s)
+    for tile in (64, 128, 256, S):
+        out = torch.empty((BH, S, S), dtype=torch.bfloat16, device="cuda")
+        cnt = torch.full((BH * S,), -1, dtype=torch.int32, device="cuda")
+        fc.fc_causal_softmax_tiles(sd, out, cnt, SCALE, tile)
+        torch.cuda.synchronize()
+        i = np.tile(np.arange(S), BH)
+        assert np.array_equal(cnt.cpu().numpy(), i // tile + 1)
+        assert np.array_equal(bits(out), run_fused(sd, BH, S, tile))
+
+
+@pytest.mark.parametrize("BH,S", [(1, 1), (2, 3), (2, 65), (1, 129), (1, 640), (2, 1000), (2, 2048)])
+def test_unfused_baseline(BH, S):
+    announce(f"softmax unfused BH={BH} S={S}")
+    s = synth.softmax_inputs(BH, S, salt=S + 2)
+    ref = oracle.causal_softmax_f64(s, SCALE)
+    out, mask = run_unfused(bf16_from_bits(s), BH, S)
+    m01 = oracle.causal_mask01(S)
+    assert np.array_equal(bf16_vals(mask), np.broadcast_to(m01, (BH, S, S)))
+    o = bf16_vals(out)
+    assert np.max(np.abs(o - ref)) <= 1e-2
+    assert np.all(o.reshape(-1, S, S)[:, m01 == 0] == 0.0)
+
+
+def test_special_rows():
+    """Row 0 is exactly [1, 0, ...]; equal scores give 1/(i+1) (bf16-rounded)."""
+    announce("softmax special rows")
+    S = 129
+    s = np.full((1, S, S), synth.f32_to_bf16_bits(np.float32(3.0)), dtype=np.uint16)
+    out = bf16_vals(run_fused(bf16_from_bits(s), 1, S, 64)).reshape(S, S)
+    assert out[0, 0] == 1.0 and np.all(out[0, 1:] == 0.0)
+    for i in range(S):
+        expect = bf16_vals(synth.f32_to_bf16_bits(np.float32(1.0 / (i + 1))))
+        assert np.all(np.abs(out[i, : i + 1] - expect) <= bf16_half_ulp(expect) * 2 + 1e-7)
+
+
+@pytest.fixture(scope="module")
+def full_scores():
+    BH, S = 128, 2048
+    announce("softmax full config: generating [8,16,2048,2048] bf16")
+    s = synth.softmax_inputs(BH, S)
+    return s, bf16_from_bits(s)
+
+
+@pytest.mark.parametrize("tile", [64, 128, 256, 2048])
+def test_full_config_sampled_rows(full_scores, tile):
+    """[8,16,2048,2048]: sampled rows against the oracle; the zero pattern and
+    row sums over the whole output."""
+    announce(f"softmax full config tile={tile}")
+    s, sd = full_scores
+    BH, S = 128, 2048
+    out = torch.empty((BH, S, S), dtype=torch.bfloat16, device="cuda")
+    fc.fc_causal_softmax(sd, out, SCALE, tile, fc.FC_SOFTMAX_FUSED)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(tile)
+    rows = np.unique(np.concatenate([rng.integers(0, BH * S, 200),
+                                     [0, 1, 63, 64, 65, 127, 128, 255, 256, 2047, 2048, BH * S - 1]]))
+    ref = oracle.causal_softmax_rows(s, SCALE, rows)
+    got = bf16_vals(bits(out.view(BH * S, S)[torch.from_numpy(rows).cuda()]))
+    assert np.max(np.abs(got - ref)) <= 1e-2
+    # properties over the whole tensor (computed on the device)
+    upper = torch.triu(torch.ones(S, S, dtype=torch.bool, device="cuda"), 1)
+    assert int((out.view(BH, S, S)[:, upper] != 0).sum()) == 0
+    sums = out.float().sum(dim=2)
+    assert float((sums - 1.0).abs().max()) <= 2e-2
+
+
+def test_full_config_unfused_sampled(full_scores):
+    announce("softmax full config unfused")
+    s, sd = full_scores
+    BH, S = 128, 2048
+    out = torch.empty((BH, S, S), dtype=torch.bfloat16, device="cuda")
+    wsb = fc.fc_softmax_workspace_bytes(BH, S, fc.FC_SOFTMAX_UNFUSED)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    fc.fc_causal_mask_materialise(ws, BH, S)
+    fc.fc_causal_softmax(sd, out, SCALE, 64, fc.FC_SOFTMAX_UNFUSED, ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 100, 2047, 2048, 70000, BH * S - 1])
+    ref = oracle.causal_softmax_rows(s, SCALE, rows)
+    got = bf16_vals(bits(out.view(BH * S, S)[torch.from_numpy(rows).cuda()]))
+    assert np.max(np.abs(got - ref)) <= 1e-2
+    del ws
