@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run one plain 1 GiB device copy before the timed region (a known-size "
+                         "kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--rows", default="chain,gemm,softmax",
                     help="comma list of row groups to run (default: all)")
     args = ap.parse_args()
@@ -247,6 +250,15 @@ def main():
             tm("softmax_unfused",
                lambda r: fc.fc_causal_softmax(sd, out, SCALE, 64, fc.FC_SOFTMAX_UNFUSED, smws))
         steps.append(sm_rows)
+
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+        del src, dst
 
     # ---------------------------------------------------------------- warmup + timed region
     tm = Timer(torch, stream)
