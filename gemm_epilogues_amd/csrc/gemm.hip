@@ -25,9 +25,34 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Epilogue operators applied after the GEMM, in chain order.
 enum { OP_BIAS = 1, OP_GELU = 2, OP_RES = 3 };
 
+// erfc by the Chebyshev fit of Press et al., Numerical Recipes, section 6.2
+// (erfcc): for z = |x|, t = 1/(1 + z/2),
+//   erfc(z) = t exp(-z^2 - 1.26551223 + t(1.00002368 + t(0.37409196 + ...)))
+// with relative error below 1.2e-7 everywhere, and erfc(-z) = 2 - erfc(z).
+// The relative accuracy carries into GELU's negative tail, where the result
+// is tiny.  About a third of the instructions of the library erff.
+__device__ __forceinline__ float erfc_cheb(float x)
+{
+    const float z = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+    float p = 0.17087277f;
+    p = __builtin_fmaf(p, t, -0.82215223f);
+    p = __builtin_fmaf(p, t, 1.48851587f);
+    p = __builtin_fmaf(p, t, -1.13520398f);
+    p = __builtin_fmaf(p, t, 0.27886807f);
+    p = __builtin_fmaf(p, t, -0.18628806f);
+    p = __builtin_fmaf(p, t, 0.09678418f);
+    p = __builtin_fmaf(p, t, 0.37409196f);
+    p = __builtin_fmaf(p, t, 1.00002368f);
+    p = __builtin_fmaf(p, t, -1.26551223f);
+    const float r = t * __builtin_amdgcn_exp2f(__builtin_fmaf(-z, z, p) * 1.4426950408889634f);
+    return x >= 0.0f ? r : 2.0f - r;
+}
+
+// GELU in erf form, z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2)) = 0.5 z erfc(-z / sqrt 2).
 __device__ __forceinline__ float gelu_erf(float z)
 {
-    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+    return 0.5f * z * erfc_cheb(-z * 0.70710678118654752f);
 }
 
 // Apply chain operators FIRST..LAST (1 = bias, 2 = gelu, 3 = residual).
@@ -233,6 +258,454 @@ __global__ __launch_bounds__(C::NT) void gemm_epi_kernel(
     }
 }
 
+// ------------------------------------------------------------------ large-tile GEMM (8 waves)
+
+// 256x256x64 workgroup tile, 8 waves (two per SIMD) each owning a 128x64
+// slice (4x2 MFMA 32x32x16 tiles, 128 fp32 accumulators).  Two waves per SIMD
+// let the hardware issue one wave's MFMAs while the other waits on LDS or the
+// barrier.  Per k16 step a wave reads 6 fragments and issues 8 MFMAs; the
+// fragments for the next step are read while the current MFMAs run
+// (double-buffered fragment registers, interleaving pinned with
+// sched_group_barrier).  The MFMA operands are swapped (B fragment first), so
+// the result tile is C^T in MFMA layout: lane l owns row m = l % 32 and four
+// consecutive columns per register quad, giving 8-byte R loads and Y stores.
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 64, NT = 512, LDK = BK + 8;
+constexpr int WN = 4;                        // wave grid 2 (M) x 4 (N)
+constexpr int WTM = 128, WTN = 64;
+constexpr int TM = WTM / 32, TN = WTN / 32;  // 4 x 2 MFMA tiles per wave
+constexpr int STAGE = (BM + BN) * LDK;       // halfs per LDS stage
+constexpr int KSTEPS = BK / 16;
+}  // namespace big
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct BigPrefetch {
+    u32x4 a[4];   // 4 A chunks of 8 halfs
+    u32x4 b[4];   // 4 rows (k) x 8 columns (n) of a B block
+    bool aok[4];  // chunk inside the matrix (only consulted when CHECKED)
+    bool bok;
+};
+
+// Global -> registers.  Addresses are clamped into the matrix, so every load
+// is valid; chunks outside are zeroed later, at store time, so no wait on the
+// loaded data is forced here.  Requires K, N % 8 == 0.
+template <bool CHECKED>
+__device__ __forceinline__ void big_load(BigPrefetch &pf, const uint16_t *__restrict__ A,
+                                         const uint16_t *__restrict__ B, int M, int N, int K,
+                                         int m0, int n0, int k0)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = t + i * big::NT;
+        const int gm = m0 + (c >> 3), gk = k0 + (c & 7) * 8;
+        pf.aok[i] = gm < M && gk < K;
+        pf.a[i] = *reinterpret_cast<const u32x4 *>(A + (int64_t)min(gm, M - 1) * K + min(gk, K - 8));
+    }
+    const int blk = t >> 1, h = t & 1;
+    const int kb = blk & 7, nb = blk >> 3;
+    const int gk = k0 + kb * 8 + h * 4, gn = n0 + nb * 8;
+    pf.bok = (k0 + kb * 8) < K && gn < N;
+    const int gnc = min(gn, N - 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        pf.b[r] = *reinterpret_cast<const u32x4 *>(B + (int64_t)min(gk + r, K - 1) * N + gnc);
+}
+
+// Registers -> LDS.  A chunks go k-contiguous; the 4x8 B block is transposed
+// into 8 columns of 4 k-values (one 8-byte write each).
+template <bool CHECKED>
+__device__ __forceinline__ void big_store(const BigPrefetch &pf, uint16_t *As, uint16_t *Bs)
+{
+    const int t = threadIdx.x;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = t + i * big::NT;
+        *reinterpret_cast<u32x4 *>(As + (c >> 3) * big::LDK + (c & 7) * 8) =
+            (!CHECKED || pf.aok[i]) ? pf.a[i] : zero;
+    }
+    u32x4 b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        b[r] = pf.b[r];
+        // opaque redefinition: keeps the transpose below (pure VALU) from being
+        // hoisted next to the global load, which would force an early wait
+        asm volatile("" : "+v"(b[r]));
+        b[r] = (!CHECKED || pf.bok) ? b[r] : zero;
+    }
+    const int blk = t >> 1, h = t & 1;
+    const int kb = blk & 7, nb = blk >> 3;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int q = c >> 1;
+        u32x2 o;
+        if (c & 1) {
+            o.x = (b[0][q] >> 16) | (b[1][q] & 0xffff0000u);
+            o.y = (b[2][q] >> 16) | (b[3][q] & 0xffff0000u);
+        } else {
+            o.x = (b[0][q] & 0xffffu) | (b[1][q] << 16);
+            o.y = (b[2][q] & 0xffffu) | (b[3][q] << 16);
+        }
+        *reinterpret_cast<u32x2 *>(Bs + (nb * 8 + c) * big::LDK + kb * 8 + h * 4) = o;
+    }
+}
+
+__device__ __forceinline__ void big_frags(const uint16_t *As, const uint16_t *Bs, int kk, int wm,
+                                          int wn, f16x8 fa[big::TM], f16x8 fb[big::TN])
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31, kq = (lane >> 5) * 8 + kk * 16;
+#pragma unroll
+    for (int i = 0; i < big::TM; ++i)
+        fa[i] = *reinterpret_cast<const f16x8 *>(As + (wm * big::WTM + i * 32 + r) * big::LDK + kq);
+#pragma unroll
+    for (int j = 0; j < big::TN; ++j)
+        fb[j] = *reinterpret_cast<const f16x8 *>(Bs + (wn * big::WTN + j * 32 + r) * big::LDK + kq);
+}
+
+template <int LAST, bool CHECKED>
+__global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * big::STAGE];
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * big::BM, n0 = tn * big::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / big::WN, wn = wave % big::WN;
+
+    f32x16 acc[big::TM][big::TN];
+#pragma unroll
+    for (int i = 0; i < big::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < big::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    BigPrefetch pf;
+    f16x8 fa[2][big::TM], fb[2][big::TN];
+    const int nk = (K + big::BK - 1) / big::BK;
+    big_load<CHECKED>(pf, A, B, M, N, K, m0, n0, 0);
+    big_store<CHECKED>(pf, lds, lds + big::BM * big::LDK);
+    __syncthreads();
+    big_frags(lds, lds + big::BM * big::LDK, 0, wm, wn, fa[0], fb[0]);
+
+    // Branch-free body: the last iteration's prefetch reads clamped (valid)
+    // addresses and lands in the stage no wave reads any more.
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t *As = lds + (kt & 1) * big::STAGE;
+        const uint16_t *Bs = As + big::BM * big::LDK;
+        uint16_t *An = lds + ((kt & 1) ^ 1) * big::STAGE;
+        big_load<CHECKED>(pf, A, B, M, N, K, m0, n0, (kt + 1) * big::BK);
+        // Each k16 step is its own scheduling region (sched_barrier fences):
+        // its 8 independent MFMAs interleave with the fragment reads of the
+        // next step (and, in step 0, the next slab's global loads; in step 3,
+        // its LDS writes), so no MFMA waits on a fragment read just issued.
+#pragma unroll
+        for (int kk = 0; kk < big::KSTEPS; ++kk) {
+            const int c = kk & 1;
+            if (kk + 1 < big::KSTEPS) big_frags(As, Bs, kk + 1, wm, wn, fa[c ^ 1], fb[c ^ 1]);
+#pragma unroll
+            for (int i = 0; i < big::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < big::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
+            if (kk == 0) {
+#pragma unroll
+                for (int s = 0; s < 6; ++s) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            } else if (kk + 1 < big::KSTEPS) {
+#pragma unroll
+                for (int s = 0; s < 6; ++s) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            } else {
+                big_store<CHECKED>(pf, An, An + big::BM * big::LDK);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        big_frags(An, An + big::BM * big::LDK, 0, wm, wn, fa[0], fb[0]);
+    }
+
+    // Epilogue.  acc[i][j] holds C^T: lane owns m = (lane % 32) of tile row i
+    // and, for register quad g, columns 8g + 4*(lane/32) .. +3 of tile column j.
+#pragma unroll
+    for (int i = 0; i < big::TM; ++i) {
+        const int m = m0 + wm * big::WTM + i * 32 + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < big::TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * big::WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (n >= N) continue;                   // N % 8 == 0: n..n+3 all valid
+                const int64_t o = (int64_t)m * N + n;
+                u32x2 bw = {0u, 0u}, rw = {0u, 0u};
+                if (LAST >= OP_BIAS) bw = *reinterpret_cast<const u32x2 *>(bias + n);
+                if (LAST >= OP_RES) rw = *reinterpret_cast<const u32x2 *>(R + o);
+                u32x2 y;
+                y.x = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 0], f16_lo(bw.x), f16_lo(rw.x)),
+                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 1], f16_hi(bw.x), f16_hi(rw.x)));
+                y.y = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 2], f16_lo(bw.y), f16_lo(rw.y)),
+                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 3], f16_hi(bw.y), f16_hi(rw.y)));
+                *reinterpret_cast<u32x2 *>(out + o) = y;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ ring GEMM (direct-to-LDS, 4 stages)
+
+// 256x256 workgroup tile, 8 waves (two per SIMD) each owning 128x64 (4x2
+// MFMA 32x32x16 tiles), K in 32-deep slabs through a 4-stage LDS ring
+// (4 x 32 KiB).  Slabs are copied global -> LDS by the direct-to-LDS load
+// (each lane's 16 bytes land at M0 + 16*lane), issued three slabs ahead, so
+// no registers stage the data and HBM latency is covered by three k-steps of
+// MFMAs.  Layouts are XOR-swizzled so every fragment read is bank-conflict
+// free:
+//   A stage: [256 rows][32 k] fp16, 64-byte rows, 16-byte k-unit u stored at
+//            u ^ ((row >> 2) & 3); fragments are ds_read_b128.
+//   B stage: [32 k][256 n] fp16 (B's own row-major layout), 32-byte n-unit v
+//            stored at v ^ (2 * (k & 3)); fragments are k-contiguous by the
+//            transposing read ds_read_b64_tr_b16: within a group of 16 lanes,
+//            lane j addresses B[k0 + j/4][n0 + 4(j%4) .. +3] and lane i gets
+//            B[k0 .. k0+3][n0 + i].
+// A whole k-step of fragments is double-buffered in registers.  Fragment
+// reads are inline asm: the compiler cannot prove they miss the in-flight
+// direct-to-LDS writes and would drain all loads before each read; ordering is
+// instead explicit (vmcnt wait for the slab's own loads, then a barrier), and
+// frag_wait*() ties the fragment registers to an lgkmcnt wait before use.
+// Needs K % 64 == 0 (an even number of slabs); M and N tails read clamped
+// rows/columns whose results are never stored.
+namespace ring {
+constexpr int BM = 256, BN = 256, BK = 32, NT = 512, S = 4, WN = 4;
+constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+constexpr int ROWB = BN * 2;                 // bytes per B k-row in LDS
+}  // namespace ring
+
+#define FC_LDS __attribute__((address_space(3)))
+#define FC_GLB __attribute__((address_space(1)))
+
+// This wave's 2 A blocks (16 rows each) and 2 B blocks (2 k-rows each) of one
+// slab, 1 KiB per direct-to-LDS instruction.
+__device__ __forceinline__ void ring_issue(const uint16_t *A, const uint16_t *B, int M, int N, int K,
+                                           int m0, int n0, int slab, FC_LDS char *st)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int k0 = slab * ring::BK;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int blk = wave * 2 + q;
+        const int row = blk * 16 + (lane >> 2);
+        const int u = (lane & 3) ^ ((lane >> 4) & 3);      // logical k-unit of this lane's slot
+        const int gm = min(m0 + row, M - 1);
+        __builtin_amdgcn_global_load_lds((const FC_GLB void *)(A + (int64_t)gm * K + k0 + u * 8),
+                                         (FC_LDS void *)(st + blk * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int blk = wave * 2 + q;
+        const int krow = blk * 2 + (lane >> 5);
+        const int p = (lane & 31) >> 1, half = lane & 1;  // physical 32-byte unit, 16-byte half
+        const int v = p ^ (2 * (krow & 3));
+        const int gn = min(n0 + v * 16 + half * 8, N - 8);
+        __builtin_amdgcn_global_load_lds((const FC_GLB void *)(B + (int64_t)(k0 + krow) * N + gn),
+                                         (FC_LDS void *)(st + ring::A_BYTES + blk * 1024), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ f16x8 lds_read_b128(uint32_t addr)
+{
+    f16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr)
+{
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// One k-step's fragments: A [k16][4 tiles], B [k16][2 tiles][2 halves of 4 k].
+struct RingFrags {
+    f16x8 a[2][4];
+    u32x2 b[2][2][2];
+};
+// Reads are issued k16-step 0 first; LDS returns in issue order, so
+// lgkmcnt(8) covers step 0 and lgkmcnt(0) covers both.
+__device__ __forceinline__ void frag_wait0(RingFrags &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(8)"
+                 : "+v"(f.a[0][0]), "+v"(f.a[0][1]), "+v"(f.a[0][2]), "+v"(f.a[0][3]),
+                   "+v"(f.b[0][0][0]), "+v"(f.b[0][0][1]), "+v"(f.b[0][1][0]), "+v"(f.b[0][1][1]));
+}
+__device__ __forceinline__ void frag_wait1(RingFrags &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[1][0]), "+v"(f.a[1][1]), "+v"(f.a[1][2]), "+v"(f.a[1][3]),
+                   "+v"(f.b[1][0][0]), "+v"(f.b[1][0][1]), "+v"(f.b[1][1][0]), "+v"(f.b[1][1][1]));
+}
+__device__ __forceinline__ f16x8 ring_bfrag(const RingFrags &f, int kk, int j)
+{
+    const u32x4 w = {f.b[kk][j][0].x, f.b[kk][j][0].y, f.b[kk][j][1].x, f.b[kk][j][1].y};
+    return __builtin_bit_cast(f16x8, w);
+}
+
+// Per-lane byte offsets, within a stage, of the 8 A and 8 B fragment reads.
+struct RingAddr {
+    uint32_t a[2][4];
+    uint32_t b[2][2][2];
+};
+__device__ __forceinline__ RingAddr ring_addr(int wm, int wn)
+{
+    RingAddr ad;
+    const int lane = threadIdx.x & 63, r = lane & 31, g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int u = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wm * 128 + i * 32 + r;
+            ad.a[kk][i] = row * 64 + (u ^ ((row >> 2) & 3)) * 16;
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            const int v = (wn * 64 + jt * 32 + 16 * (g & 1)) >> 4;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int k = kk * 16 + 8 * (g >> 1) + 4 * hh + (j >> 2);
+                ad.b[kk][jt][hh] = ring::A_BYTES + k * ring::ROWB + (v ^ (2 * (k & 3))) * 32 + (j & 3) * 8;
+            }
+        }
+    }
+    return ad;
+}
+
+template <int LAST>
+__global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_raw[ring::S * ring::STAGE];
+    FC_LDS char *lds = (FC_LDS char *)lds_raw;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * ring::BM, n0 = tn * ring::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / ring::WN, wn = wave % ring::WN;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = K / ring::BK;                 // even
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    const RingAddr ad = ring_addr(wm, wn);
+    for (int s = 0; s < ring::S - 1; ++s)
+        ring_issue(A, B, M, N, K, m0, n0, min(s, nk - 1), lds + s * ring::STAGE);
+    __builtin_amdgcn_s_waitcnt(0xF78);           // vmcnt(8): slab 0 of this wave landed
+    __builtin_amdgcn_s_barrier();                // ... and of every wave
+    RingFrags F[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) F[0].a[kk][i] = lds_read_b128(lds0 + ad.a[kk][i]);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) F[0].b[kk][jt][hh] = lds_read_tr16(lds0 + ad.b[kk][jt][hh]);
+    }
+    for (int t = 0; t < nk; t += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {            // register buffer index stays static
+            const int tt = t + h, cb = h, nb = h ^ 1;
+            frag_wait0(F[cb]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 0, j), F[cb].a[0][i],
+                                                                       acc[i][j], 0, 0, 0);
+            // slab tt+3 goes to the stage read for step tt-1, which every wave
+            // finished before the previous barrier; past the end a clamped
+            // re-read lands in a stage that is never read
+            ring_issue(A, B, M, N, K, m0, n0, min(tt + ring::S - 1, nk - 1),
+                       lds + ((tt + ring::S - 1) % ring::S) * ring::STAGE);
+            __builtin_amdgcn_s_waitcnt(0xF78);   // vmcnt(8): slab tt+1 of this wave landed
+            __builtin_amdgcn_s_barrier();        // ... and of every wave
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t st = lds0 + ((tt + 1) % ring::S) * ring::STAGE;
+            frag_wait1(F[cb]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = q >> 1, j = q & 1;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 1, j), F[cb].a[1][i],
+                                                                   acc[i][j], 0, 0, 0);
+                const int kk = q >> 2, rr = q & 3;   // next step's k16-step-0 frags first
+                F[nb].a[kk][rr] = lds_read_b128(st + ad.a[kk][rr]);
+                F[nb].b[kk][rr >> 1][rr & 1] = lds_read_tr16(st + ad.b[kk][rr >> 1][rr & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);           // drain the clamped prefetches
+    frag_wait0(F[0]);
+    frag_wait1(F[0]);
+
+    // Epilogue on the accumulators (C^T layout: lane owns row m = lane % 32 of
+    // tile row i and columns 8g + 4*(lane/32) .. +3 of tile column j).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (n >= N) continue;
+                const int64_t o = (int64_t)m * N + n;
+                u32x2 bw = {0u, 0u}, rw = {0u, 0u};
+                if (LAST >= OP_BIAS) bw = *reinterpret_cast<const u32x2 *>(bias + n);
+                if (LAST >= OP_RES) rw = *reinterpret_cast<const u32x2 *>(R + o);
+                u32x2 y;
+                y.x = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 0], f16_lo(bw.x), f16_lo(rw.x)),
+                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 1], f16_hi(bw.x), f16_hi(rw.x)));
+                y.y = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 2], f16_lo(bw.y), f16_lo(rw.y)),
+                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 3], f16_hi(bw.y), f16_hi(rw.y)));
+                *reinterpret_cast<u32x2 *>(out + o) = y;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ skinny GEMM (M <= 16)
 
 // Decode shape: one workgroup per 16-column strip of the output; its waves
@@ -329,7 +802,6 @@ __global__ __launch_bounds__(256) void epi_pointwise_kernel(const uint16_t *in,
 
 // ------------------------------------------------------------------ host
 
-using CfgBig = GemmCfg<256, 256, 64, 2, 2>;     // 4 waves, 128x128 per wave
 using CfgMid = GemmCfg<128, 128, 64, 2, 2>;     // 4 waves, 64x64 per wave
 constexpr int kSkinnyWaves = 8;
 
@@ -355,7 +827,22 @@ static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bia
     }
     // large problems: 256x256 tiles; smaller ones: 128x128 (more workgroups)
     const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (big_tiles >= 128) return launch_gemm_cfg<CfgBig, LAST>(A, B, bias, R, out, M, N, K, s);
+    if (big_tiles >= 128) {
+        const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
+        if (K % 64 == 0) {
+            gemm_ring_kernel<LAST><<<tiles_m * tiles_n, ring::NT, 0, s>>>(A, B, bias, R, out, M, N, K,
+                                                                         tiles_m, tiles_n);
+            return launch_status();
+        }
+        const bool interior = M % big::BM == 0 && N % big::BN == 0 && K % big::BK == 0;
+        if (interior)
+            gemm_big_kernel<LAST, false><<<tiles_m * tiles_n, big::NT, 0, s>>>(A, B, bias, R, out, M, N, K,
+                                                                              tiles_m, tiles_n);
+        else
+            gemm_big_kernel<LAST, true><<<tiles_m * tiles_n, big::NT, 0, s>>>(A, B, bias, R, out, M, N, K,
+                                                                             tiles_m, tiles_n);
+        return launch_status();
+    }
     return launch_gemm_cfg<CfgMid, LAST>(A, B, bias, R, out, M, N, K, s);
 }
 

@@ -129,3 +129,42 @@ def test_square_4096_config_sampled():
     # plans differ only by fp16 rounding at the cuts
     for p, y in ys.items():
         assert np.max(np.abs(y - ys[(4,)]) / (1 + np.abs(ys[(4,)]))) <= 1e-2, p
+
+
+def test_ring_path_ragged_all_plans():
+    """K % 64 == 0 and >= 128 tiles: the direct-to-LDS ring kernel, with M and N
+    tails (clamped rows/columns are computed but never stored)."""
+    M, N, K = 2085, 4136, 320
+    announce(f"gemm ring path M={M} N={N} K={K}")
+    d = Dev(M, N, K, salt=11)
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([rng.integers(0, M, 3000), [0, M - 1, 2047, 2048, 255, 256]])
+    cols = np.concatenate([rng.integers(0, N, 3000), [0, N - 1, 4095, 4096, 255, 256]])
+    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
+    for plan in ALL_PLANS:
+        Y = d.run(plan)
+        ok, worst = tol_ok(Y[rows, cols], ref)
+        assert ok, (plan, worst)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 64), (300, 520, 64), (4096, 4096, 64)])
+def test_gelu_epilogue_accuracy(M, N, K):
+    """A = 0 and R = 0 give Y = fp16(GELU(bias)) exactly up to the final
+    rounding: every plan's GELU (fused on the accumulators or pointwise) is
+    within one fp16 ulp of the fp64 oracle, for bias spanning [-8, 8]."""
+    announce(f"gelu accuracy M={M} N={N} K={K}")
+    A = np.zeros((M, K), np.uint16)
+    B = synth.gemm_inputs(8, N, K, salt=1)[1]
+    zs = np.linspace(-8.0, 8.0, N)
+    bias = synth.f64_to_f16_bits(zs)
+    R = np.zeros((M, N), np.uint16)
+    d = Dev(1, 8, 8)
+    d.M, d.N, d.K = M, N, K
+    d.h = (A, B, bias, R)
+    d.A, d.B, d.bias, d.R = (f16_from_bits(x) for x in d.h)
+    ref = oracle.gemm_epilogue_f64(A[:1], B, bias, R[:1])[0]
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    for plan in ALL_PLANS:
+        Y = d.run(plan).view(np.float16).astype(np.float64)
+        assert np.all(Y == Y[0]), plan
+        assert np.all(np.abs(Y[0] - ref) <= ulp + 1e-12), (plan, float(np.max(np.abs(Y[0] - ref) / ulp)))
