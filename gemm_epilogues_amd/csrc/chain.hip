@@ -9,6 +9,11 @@
 
 namespace fc {
 
+// Each workgroup streams one contiguous chunk of kChainBlock * kChainVecs
+// fp32x4 vectors: all kChainVecs loads of a lane are issued before any
+// store, lanes interleave within each 4 KiB run, and at n = 16M the whole
+// grid (2048 workgroups, 8 per CU) is resident at once, so there is no tail
+// round.
 template <int K, bool RELU>
 __global__ __launch_bounds__(kChainBlock) void chain_fused_kernel(const float *__restrict__ x,
                                                                   float *__restrict__ y, int64_t n,
@@ -17,20 +22,17 @@ __global__ __launch_bounds__(kChainBlock) void chain_fused_kernel(const float *_
     const int64_t nvec = n >> 2;
     const f32x4 *xv = reinterpret_cast<const f32x4 *>(x);
     f32x4 *yv = reinterpret_cast<f32x4 *>(y);
-    const int64_t stride = (int64_t)gridDim.x * kChainBlock;
-    for (int64_t base = (int64_t)blockIdx.x * kChainBlock + threadIdx.x; base < nvec;
-         base += stride * kChainUnroll) {
-        f32x4 v[kChainUnroll];
+    const int64_t base = (int64_t)blockIdx.x * kChainBlock * kChainVecs + threadIdx.x;
+    f32x4 v[kChainVecs];
 #pragma unroll
-        for (int u = 0; u < kChainUnroll; ++u) {
-            int64_t i = base + u * stride;
-            if (i < nvec) v[u] = __builtin_nontemporal_load(xv + i);
-        }
+    for (int u = 0; u < kChainVecs; ++u) {
+        const int64_t i = base + u * kChainBlock;
+        if (i < nvec) v[u] = __builtin_nontemporal_load(xv + i);
+    }
 #pragma unroll
-        for (int u = 0; u < kChainUnroll; ++u) {
-            int64_t i = base + u * stride;
-            if (i < nvec) __builtin_nontemporal_store(chain_vec<K, RELU>(v[u], c), yv + i);
-        }
+    for (int u = 0; u < kChainVecs; ++u) {
+        const int64_t i = base + u * kChainBlock;
+        if (i < nvec) __builtin_nontemporal_store(chain_vec<K, RELU>(v[u], c), yv + i);
     }
     chain_tail<K, RELU>(x, y, n, c);
 }
@@ -43,26 +45,23 @@ __global__ __launch_bounds__(kChainBlock) void chain_stage_kernel(const float *_
     const f32x4 *xv = reinterpret_cast<const f32x4 *>(x);
     f32x4 *yv = reinterpret_cast<f32x4 *>(y);
     const bool r = relu != 0;
-    const int64_t stride = (int64_t)gridDim.x * kChainBlock;
-    for (int64_t base = (int64_t)blockIdx.x * kChainBlock + threadIdx.x; base < nvec;
-         base += stride * kChainUnroll) {
-        f32x4 v[kChainUnroll];
+    const int64_t base = (int64_t)blockIdx.x * kChainBlock * kChainVecs + threadIdx.x;
+    f32x4 v[kChainVecs];
 #pragma unroll
-        for (int u = 0; u < kChainUnroll; ++u) {
-            int64_t i = base + u * stride;
-            if (i < nvec) v[u] = __builtin_nontemporal_load(xv + i);
-        }
+    for (int u = 0; u < kChainVecs; ++u) {
+        const int64_t i = base + u * kChainBlock;
+        if (i < nvec) v[u] = __builtin_nontemporal_load(xv + i);
+    }
 #pragma unroll
-        for (int u = 0; u < kChainUnroll; ++u) {
-            int64_t i = base + u * stride;
-            if (i < nvec) {
-                f32x4 w = v[u];
-                w.x = stage_scalar(w.x, a, b, r);
-                w.y = stage_scalar(w.y, a, b, r);
-                w.z = stage_scalar(w.z, a, b, r);
-                w.w = stage_scalar(w.w, a, b, r);
-                __builtin_nontemporal_store(w, yv + i);
-            }
+    for (int u = 0; u < kChainVecs; ++u) {
+        const int64_t i = base + u * kChainBlock;
+        if (i < nvec) {
+            f32x4 w = v[u];
+            w.x = stage_scalar(w.x, a, b, r);
+            w.y = stage_scalar(w.y, a, b, r);
+            w.z = stage_scalar(w.z, a, b, r);
+            w.w = stage_scalar(w.w, a, b, r);
+            __builtin_nontemporal_store(w, yv + i);
         }
     }
     int64_t t = (n & ~int64_t(3)) + threadIdx.x;
@@ -71,21 +70,16 @@ __global__ __launch_bounds__(kChainBlock) void chain_stage_kernel(const float *_
 
 // ------------------------------------------------------------------ host
 
-static int grid_for(int64_t nvec, int max_blocks)
+static int64_t grid_for(int64_t nvec)
 {
-    int64_t want = ceil_div(nvec, (int64_t)kChainBlock * kChainUnroll);
-    if (want < 1) want = 1;
-    if (want > max_blocks) want = max_blocks;
-    return (int)want;
+    int64_t g = ceil_div(nvec, (int64_t)kChainBlock * kChainVecs);
+    return g < 1 ? 1 : g;
 }
-
-static constexpr int kFusedMaxBlocks = 1 << 20;
 
 template <int K, bool RELU>
 static void launch_fused(const float *x, float *y, int64_t n, const ChainCoef &c, hipStream_t s)
 {
-    int grid = grid_for(n >> 2, kFusedMaxBlocks);
-    chain_fused_kernel<K, RELU><<<grid, kChainBlock, 0, s>>>(x, y, n, c);
+    chain_fused_kernel<K, RELU><<<(unsigned)grid_for(n >> 2), kChainBlock, 0, s>>>(x, y, n, c);
 }
 
 template <bool RELU>
@@ -124,6 +118,7 @@ extern "C" int fc_chain(const float *x, float *y, int64_t n, const float *a, con
                         int relu_even, int mode, float *scratch, int fat_temps, fc_stream stream)
 {
     if (n < 0) return FC_ERR_SHAPE;
+    if ((n >> 2) / ((int64_t)kChainBlock * kChainVecs) >= 0x7fffffff) return FC_ERR_UNSUPPORTED;
     if (K < 1 || K > FC_CHAIN_MAX_STAGES) return FC_ERR_UNSUPPORTED;
     if (mode != FC_CHAIN_NAIVE && mode != FC_CHAIN_FUSED && mode != FC_CHAIN_FAT)
         return FC_ERR_UNSUPPORTED;
@@ -146,7 +141,7 @@ extern "C" int fc_chain(const float *x, float *y, int64_t n, const float *a, con
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (mode == FC_CHAIN_NAIVE) {
         // stage s writes y when (K-1-s) is even, else scratch: the last lands in y
-        const int grid = grid_for(n >> 2, kFusedMaxBlocks);
+        const unsigned grid = (unsigned)grid_for(n >> 2);
         const float *in = x;
         for (int st = 0; st < K; ++st) {
             float *out = ((K - 1 - st) % 2 == 0) ? y : scratch;

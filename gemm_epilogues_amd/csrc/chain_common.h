@@ -13,7 +13,8 @@ struct ChainCoef {
 };
 
 constexpr int kChainBlock = 256;
-constexpr int kChainUnroll = 4;
+constexpr int kChainUnroll = 4;     // fat probe: vectors in flight per lane
+constexpr int kChainVecs = 8;       // fused / naive: contiguous vectors per lane
 
 template <int K, bool RELU>
 __device__ __forceinline__ float chain_scalar(float v, const ChainCoef &c)

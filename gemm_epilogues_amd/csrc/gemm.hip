@@ -772,6 +772,108 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     }
 }
 
+// ------------------------------------------------------------------ decode GEMM (M <= 16, streams B)
+
+// At M <= 16 the GEMM is a stream over B (K x N fp16).  One workgroup per
+// 16-column strip, strips remapped so the workgroups of one XCD stream a
+// contiguous band of columns (their 32-byte row pieces share the XCD's L2
+// lines).  The 8 waves split K into 32-deep k-steps (at most 16 per wave).
+// A wave loads its A fragments (16 rows x its k-range, at most 64 VGPRs)
+// straight into registers, and streams its B rows through its own ring of 16
+// one-KiB LDS stages filled by direct-to-LDS loads fifteen steps ahead (no
+// barriers: a wave only reads what it loaded), so the whole of B is in flight
+// at once.  B stage layout: [32 k][16 n], k-row k in 32-byte slot
+// k ^ (4 * ((k >> 3) & 1)), read k-contiguous with ds_read_b64_tr_b16.  One
+// v_mfma_f32_16x16x32_f16 per k-step; the wave partials are summed through
+// LDS, then the epilogue, then the store.  Needs N % 16 == 0,
+// K % 256 == 0 and K <= 4096.
+namespace dec {
+constexpr int WAVES = 8, NT = WAVES * 64, S = 16, STAGE = 1024, KSTEP = 32, MAXSTEPS = 16;
+}
+
+__device__ __forceinline__ void dec_issue_b(const uint16_t *B, int N, int n0, int k0, FC_LDS char *st)
+{
+    const int lane = threadIdx.x & 63;
+    const int slot = lane >> 1, half = lane & 1;
+    const int k = slot ^ (4 * ((slot >> 3) & 1));
+    __builtin_amdgcn_global_load_lds((const FC_GLB void *)(B + (int64_t)(k0 + k) * N + n0 + half * 8),
+                                     (FC_LDS void *)st, 16, 0, 0);
+}
+
+template <int LAST>
+__global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
+    int M, int N, int K)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_raw[dec::WAVES * dec::S * dec::STAGE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = gridDim.x;
+    int strip = blockIdx.x;
+    if (G % 8 == 0) strip = (strip % 8) * (G / 8) + strip / 8;
+    const int n0 = strip * 16;
+    FC_LDS char *ring = (FC_LDS char *)lds_raw + wave * dec::S * dec::STAGE;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+    const int kper = K / dec::WAVES, nsteps = kper / dec::KSTEP, kbase = wave * kper;
+    const int g = lane >> 4, i = lane & 15;
+
+    // A fragments of every k-step (16x16x32 A operand: row i, k = 8g .. 8g+7),
+    // loaded in inline asm so they are issued here, before the ring prologue:
+    // VMEM loads complete in order, so the per-step vmcnt wait below (which
+    // ties the step's A fragment) also covers them.
+    f16x8 afr[dec::MAXSTEPS];
+    const uint16_t *arow = A + (int64_t)min(i, M - 1) * K + kbase + 8 * g;
+#pragma unroll
+    for (int t = 0; t < dec::MAXSTEPS; ++t) {
+        const uint16_t *src = arow + min(t, nsteps - 1) * dec::KSTEP;
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(afr[t]) : "v"(src));
+    }
+
+    uint32_t b_off[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int k = 8 * g + 4 * hh + (i >> 2);
+        b_off[hh] = (uint32_t)((k ^ (4 * ((k >> 3) & 1))) * 32 + (i & 3) * 8);
+    }
+#pragma unroll
+    for (int s = 0; s < dec::S - 1; ++s)
+        dec_issue_b(B, N, n0, kbase + min(s, nsteps - 1) * dec::KSTEP, ring + s * dec::STAGE);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < dec::MAXSTEPS; ++t) {
+        if (t < nsteps) {
+            dec_issue_b(B, N, n0, kbase + min(t + dec::S - 1, nsteps - 1) * dec::KSTEP,
+                        ring + ((t + dec::S - 1) % dec::S) * dec::STAGE);
+            asm volatile("s_waitcnt vmcnt(15)" : "+v"(afr[t]));   // stage t (and every A load) landed
+            const uint32_t st = ring0 + (t % dec::S) * dec::STAGE;
+            u32x2 b0 = lds_read_tr16(st + b_off[0]);
+            u32x2 b1 = lds_read_tr16(st + b_off[1]);
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b0), "+v"(b1));
+            const u32x4 bw = {b0.x, b0.y, b1.x, b1.y};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[t], __builtin_bit_cast(f16x8, bw), acc, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);           // drain the clamped prefetches
+    __syncthreads();                             // every wave done with its ring
+    // 16x16 result layout: lane holds column (lane % 16), rows 4*(lane/16) + r
+    float *part = (float *)lds_raw;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave * 256 + (4 * g + r) * 16 + i] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int e = threadIdx.x, row = e >> 4, col = n0 + (e & 15);
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < dec::WAVES; ++w) v += part[w * 256 + e];
+        if (row < M) {
+            const int64_t o = (int64_t)row * N + col;
+            const float bv = (LAST >= OP_BIAS) ? h2f(bias[col]) : 0.0f;
+            const float rv = (LAST >= OP_RES) ? h2f(R[o]) : 0.0f;
+            out[o] = f2h(apply_ops<OP_BIAS, LAST>(v, bv, rv));
+        }
+    }
+}
+
 // ------------------------------------------------------------------ pointwise segments
 
 // Operators FIRST..LAST on an fp16 [M,N] intermediate; out may equal in.
@@ -820,6 +922,11 @@ template <int LAST>
 static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
                        uint16_t *out, int M, int N, int K, hipStream_t s)
 {
+    if (M <= 16 && K % (dec::WAVES * dec::KSTEP) == 0 && K <= dec::WAVES * dec::KSTEP * dec::MAXSTEPS &&
+        N % 16 == 0) {
+        gemm_decode_kernel<LAST><<<N / 16, dec::NT, 0, s>>>(A, B, bias, R, out, M, N, K);
+        return launch_status();
+    }
     if (M <= 16) {
         gemm_skinny_kernel<kSkinnyWaves, LAST><<<(N + 15) / 16, kSkinnyWaves * 64, 0, s>>>(
             A, B, bias, R, out, M, N, K);
