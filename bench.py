@@ -58,20 +58,40 @@ def log(msg):
 
 
 class Timer:
-    """Event pairs on the launch stream; elapsed times collected per row."""
+    """Event pairs on the launch stream; elapsed times collected per row.
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream = torch, stream
+    A row is `reps` calls of the binding, launched from the host as they come
+    (the host runs ahead of the GPU, so kernels follow each other without
+    gaps).  With graph=True the first run of a row captures its calls into a
+    HIP graph and from then on the row is one graph replay between the two
+    events; on this stack that adds one to two microseconds per kernel node, so
+    it is not the default."""
+
+    def __init__(self, torch, stream, graph=False):
+        self.torch, self.stream, self.eager = torch, stream, not graph
         self.pending = []
         self.ms = {}
+        self.graphs = {}
 
     def __call__(self, name, fn, reps=1):
         t = self.torch
+        g = None
+        if not self.eager:
+            g = self.graphs.get(name)
+            if g is None:
+                g = t.cuda.CUDAGraph()
+                with t.cuda.graph(g):
+                    for r in range(reps):
+                        fn(r)
+                self.graphs[name] = g
         e0 = t.cuda.Event(enable_timing=True)
         e1 = t.cuda.Event(enable_timing=True)
         e0.record(self.stream)
-        for r in range(reps):
-            fn(r)
+        if g is not None:
+            g.replay()
+        else:
+            for r in range(reps):
+                fn(r)
         e1.record(self.stream)
         self.pending.append((name, e0, e1, reps))
 
@@ -172,6 +192,8 @@ def main():
                          "kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--rows", default="chain,affine,decode,gemm,softmax",
                     help="comma list of row groups to run (default: all)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time each row as one replay of a HIP graph captured from its calls")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -214,14 +236,13 @@ def main():
                 tm(f"chain_fused_K{K}",
                    lambda r, a=a, b=b: fc.fc_chain(sets[r][0], sets[r][1], a, b, True,
                                                    fc.FC_CHAIN_FUSED), reps=CHAIN_SETS)
-                st = sets[step_i % CHAIN_SETS]
                 tm(f"chain_naive_K{K}",
-                   lambda r, a=a, b=b, st=st: fc.fc_chain(st[0], st[1], a, b, True,
-                                                          fc.FC_CHAIN_NAIVE, st[2]))
+                   lambda r, a=a, b=b: fc.fc_chain(sets[r][0], sets[r][1], a, b, True,
+                                                   fc.FC_CHAIN_NAIVE, sets[r][2]), reps=CHAIN_SETS)
             a, b = coef[FAT_K]
-            st = sets[(step_i + 1) % CHAIN_SETS]
             tm(f"chain_fat_K{FAT_K}_T{FAT_T}",
-               lambda r: fc.fc_chain(st[0], st[1], a, b, True, fc.FC_CHAIN_FAT, sink, FAT_T))
+               lambda r: fc.fc_chain(sets[r][0], sets[r][1], a, b, True, fc.FC_CHAIN_FAT, sink, FAT_T),
+               reps=CHAIN_SETS)
         steps.append(chain_rows)
 
     if "affine" in groups:
@@ -247,8 +268,10 @@ def main():
         for r in range(DECODE_SETS):
             A, B, bias, R = synth.gemm_inputs(M, N, K, salt=r)
             tdv = [torch.from_numpy(v.view(np.int16)).to(dev).view(torch.float16) for v in (A, B, bias, R)]
+            # one zero-filled workspace serves every plan of a shape
+            wsb = max(fc.fc_gemm_workspace_bytes(M, N, K, p) for p in PLANS)
             dsets.append(tdv + [torch.empty((M, N), dtype=torch.float16, device=dev),
-                                torch.empty(M * N, dtype=torch.float16, device=dev)])
+                                torch.zeros(wsb, dtype=torch.uint8, device=dev)])
 
         def decode_rows(tm, step_i):
             for plan in PLANS:
@@ -263,7 +286,8 @@ def main():
         A, B, bias, R = synth.gemm_inputs(M, N, K)
         td = [torch.from_numpy(v.view(np.int16)).to(dev).view(torch.float16) for v in (A, B, bias, R)]
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-        ws = torch.empty(M * N, dtype=torch.float16, device=dev)
+        ws = torch.zeros(max(fc.fc_gemm_workspace_bytes(M, N, K, p) for p in PLANS), dtype=torch.uint8,
+                         device=dev)
 
         def gemm_rows(tm, step_i):
             for plan in PLANS:
@@ -301,7 +325,7 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- warmup + timed region
-    tm = Timer(torch, stream)
+    tm = Timer(torch, stream, graph=args.graph)
     log(f"warmup {args.warmup} steps")
     for w in range(args.warmup):
         for f in steps:
@@ -430,6 +454,16 @@ def main():
                        "algorithmic_flops": fl,
                        "traffic": load_traffic("gemm_plan4",
                                                os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "gemm.hip"))})
+    if "decode" in groups:
+        M, N, K = DECODE_MNK
+        b = fc.fc_plan_bytes(M, N, K, [4])
+        t = tm.median("decode_plan4") * 1e-3
+        others.append({"bound": "hbm", "kernel": "gemm_decode_kernel<bias+gelu+res> 16x4096x4096 plan [4]",
+                       "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 2),
+                       "algorithmic_bytes": b,
+                       "traffic": load_traffic("decode_plan4",
+                                               os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "gemm.hip"))})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -452,7 +486,10 @@ def main():
         "config": {
             "workload": ("fused pointwise chain n=16,777,216 fp32 K in {2,3,4,6,8} (naive, fused, fat K=4 T=48) "
                          "+ causal scaled softmax [8,16,2048,2048] bf16 (fused tiles 64/128/256/none, unfused "
-                         "5-pass + mask) + GEMM+bias+GELU+residual 4096^3 fp16 plans [1,1,1,1],[1,3],[2,2],[4]"),
+                         "5-pass + mask) + GEMM+bias+GELU+residual 4096^3 and 16x4096x4096 fp16 plans "
+                         "[1,1,1,1],[1,3],[2,2],[4] + affine chain n=1,048,576 K=8"),
+            "timing": ("HIP event pair per row around " +
+                       ("one replay of the row's captured HIP graph" if args.graph else "host launches")),
             "value_definition": "algorithmic bytes of fused chain (K=2,3,4,6,8) + fused softmax (tile 64) / their summed kernel time",
             "gemm_TFLOPs_plan4": comp.get("gemm_plan4", {}).get("TFLOPs"),
             "device": props.name,

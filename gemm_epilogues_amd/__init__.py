@@ -38,7 +38,7 @@ FC_SOFTMAX_UNFUSED = 1
 FC_CHAIN_MAX_STAGES = 32
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m gemm_epilogues_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built: run `python gemm_epilogues_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 # torch ships its own HIP runtime with the same SONAME (libamdhip64.so.7) as
@@ -203,7 +203,10 @@ def fc_gemm_workspace_bytes(M: int, N: int, K: int, plan: Sequence[int]) -> int:
 
 
 def fc_gemm_epilogue(A, B, bias, R, Y, plan: Sequence[int], workspace=None, stream=None) -> None:
-    """Y = GELU(A@B + bias) + R, fp16 device tensors A [M,K], B [K,N], bias [N], R/Y [M,N]."""
+    """Y = GELU(A@B + bias) + R, fp16 device tensors A [M,K], B [K,N], bias [N], R/Y [M,N].
+
+    A caller-supplied workspace must be zero-filled before its first use (see
+    fc_gemm_workspace_bytes); without one, a zero-filled one is allocated."""
     torch = _torch()
     for t, nm in ((A, "A"), (B, "B"), (bias, "bias"), (R, "R"), (Y, "Y")):
         _dev(t, torch.float16, nm)
@@ -215,6 +218,11 @@ def fc_gemm_epilogue(A, B, bias, R, Y, plan: Sequence[int], workspace=None, stre
         raise ValueError("shape mismatch")
     arr, n = _int_array(plan)
     ws_bytes = 0
+    if workspace is None:
+        need = int(_lib.fc_gemm_workspace_bytes(M, N, K, arr, n))
+        if need:
+            # zero-filled, as the decode kernel's arrival counters require
+            workspace = torch.zeros(need, dtype=torch.uint8, device=A.device)
     if workspace is not None:
         if not workspace.is_cuda:
             raise ValueError("workspace must be a device tensor")

@@ -5,7 +5,7 @@ then linked into one shared library exporting the C ABI of include/fc.h.  The
 compiler's per-kernel resource report (VGPRs, AGPRs, SGPRs, LDS, scratch,
 occupancy) is parsed into kernel_resources.json next to the library.
 
-Usage: python -m gemm_epilogues_amd.build [--jobs N]
+Usage: python gemm_epilogues_amd/build.py [--jobs N]
 """
 from __future__ import annotations
 

@@ -772,106 +772,212 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     }
 }
 
-// ------------------------------------------------------------------ decode GEMM (M <= 16, streams B)
+// ------------------------------------------------------------------ decode GEMM (M <= 16, split K)
 
-// At M <= 16 the GEMM is a stream over B (K x N fp16).  One workgroup per
-// 16-column strip, strips remapped so the workgroups of one XCD stream a
-// contiguous band of columns (their 32-byte row pieces share the XCD's L2
-// lines).  The 8 waves split K into 32-deep k-steps (at most 16 per wave).
-// A wave loads its A fragments (16 rows x its k-range, at most 64 VGPRs)
-// straight into registers, and streams its B rows through its own ring of 16
-// one-KiB LDS stages filled by direct-to-LDS loads fifteen steps ahead (no
-// barriers: a wave only reads what it loaded), so the whole of B is in flight
-// at once.  B stage layout: [32 k][16 n], k-row k in 32-byte slot
-// k ^ (4 * ((k >> 3) & 1)), read k-contiguous with ds_read_b64_tr_b16.  One
-// v_mfma_f32_16x16x32_f16 per k-step; the wave partials are summed through
-// LDS, then the epilogue, then the store.  Needs N % 16 == 0,
-// K % 256 == 0 and K <= 4096.
+// At M <= 16 the GEMM is a stream over B (K x N fp16), so the layout is
+// chosen for the stream: every workgroup owns a 64-column strip of B (one
+// full 128-byte line per k-row) and a 1/P share of K, and requests its whole
+// slab (at most 1024 k-rows, 128 KiB) at once with direct-to-LDS loads; its 8
+// waves each take a contiguous eighth of the slab and read only what they
+// loaded, so no barrier sits between the loads and the MFMAs.  B slab layout
+// per wave: k-row k at 128 k bytes, 16-byte unit u at u ^ dec_swz(k), which
+// spreads the transposing reads (ds_read_b64_tr_b16, four k-rows per
+// 16-lane group) over all banks.  A fragments (16 rows x the wave's k-range)
+// go straight to registers.  One v_mfma_f32_16x16x32_f16 per 32-deep k-step
+// and 16-column tile.
+//
+// The eight wave partials are summed through LDS in wave order.  With P = 1
+// the workgroup applies the epilogue and stores Y.  With P > 1 it publishes its
+// 16x64 fp32 partial to the workspace and takes a ticket from the strip's
+// arrival counter; the workgroup that draws the last ticket sums the P
+// partials in split order (so the result does not depend on arrival order),
+// applies the epilogue, stores Y and puts the counter back to zero.  No
+// workgroup ever waits for another, so the launch needs no co-residency.
+//
+// Visibility across XCDs without a full L2 write-back: partials are written
+// with device-scope stores (they write through to the device coherence point
+// and count as complete only once there), every thread waits for its stores
+// before the workgroup barrier that precedes the ticket, and the last
+// workgroup reads the partials with device-scope loads, which are served from
+// the coherence point rather than a possibly stale line of its own XCD's L2.
 namespace dec {
-constexpr int WAVES = 8, NT = WAVES * 64, S = 16, STAGE = 1024, KSTEP = 32, MAXSTEPS = 16;
+constexpr int WAVES = 8, NT = WAVES * 64, W = 64, ROW = W * 2, KSTEP = 32, MAXSTEPS = 4;
+constexpr int TILE = 16 * W;                                     // outputs per strip
+constexpr int MAXP = 64;
+constexpr int MAX_LDS = WAVES * KSTEP * MAXSTEPS * ROW;          // 128 KiB
 }
 
-__device__ __forceinline__ void dec_issue_b(const uint16_t *B, int N, int n0, int k0, FC_LDS char *st)
+__device__ __forceinline__ int dec_swz(int k) { return 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1); }
+
+// Epilogue of one output pair (row, col), (row, col+1): bw and rw are the
+// fp16 pairs of bias and R, loaded at kernel start.
+template <int LAST>
+__device__ __forceinline__ void dec_store_pair(uint16_t *__restrict__ out, int N, int row, int col, uint32_t bw,
+                                               uint32_t rw, float v0, float v1)
 {
-    const int lane = threadIdx.x & 63;
-    const int slot = lane >> 1, half = lane & 1;
-    const int k = slot ^ (4 * ((slot >> 3) & 1));
-    __builtin_amdgcn_global_load_lds((const FC_GLB void *)(B + (int64_t)(k0 + k) * N + n0 + half * 8),
-                                     (FC_LDS void *)st, 16, 0, 0);
+    *reinterpret_cast<uint32_t *>(out + (int64_t)row * N + col) =
+        pack_f16x2(apply_ops<OP_BIAS, LAST>(v0, f16_lo(bw), f16_lo(rw)),
+                   apply_ops<OP_BIAS, LAST>(v1, f16_hi(bw), f16_hi(rw)));
 }
 
 template <int LAST>
 __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
-    int M, int N, int K)
+    int M, int N, int K, int P, uint32_t *__restrict__ counters, float *__restrict__ partials)
 {
-    __shared__ __attribute__((aligned(1024))) char lds_raw[dec::WAVES * dec::S * dec::STAGE];
+    extern __shared__ __attribute__((aligned(1024))) char dec_lds[];
+    __shared__ int is_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a run of
+    // consecutive (strip, split) pairs so the splits of one strip, and the A
+    // slices they share, stay in one L2.
     const int G = gridDim.x;
-    int strip = blockIdx.x;
-    if (G % 8 == 0) strip = (strip % 8) * (G / 8) + strip / 8;
-    const int n0 = strip * 16;
-    FC_LDS char *ring = (FC_LDS char *)lds_raw + wave * dec::S * dec::STAGE;
-    const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
-    const int kper = K / dec::WAVES, nsteps = kper / dec::KSTEP, kbase = wave * kper;
+    int b = blockIdx.x;
+    if (G % 8 == 0) b = (b % 8) * (G / 8) + b / 8;
+    const int strip = b / P, split = b - strip * P;
+    const int n0 = strip * dec::W;
+    const int kw = K / (P * dec::WAVES);                          // k-rows per wave, multiple of 32
+    const int kbase = split * (K / P) + wave * kw;
+    const int nsteps = kw / dec::KSTEP;
+    FC_LDS char *slab = (FC_LDS char *)dec_lds + wave * kw * dec::ROW;
+    const uint32_t slab0 = (uint32_t)(uintptr_t)slab;
     const int g = lane >> 4, i = lane & 15;
 
-    // A fragments of every k-step (16x16x32 A operand: row i, k = 8g .. 8g+7),
-    // loaded in inline asm so they are issued here, before the ring prologue:
-    // VMEM loads complete in order, so the per-step vmcnt wait below (which
-    // ties the step's A fragment) also covers them.
+    // the output pair this thread stores if its workgroup finishes the strip:
+    // bias and R are fetched now, off the critical tail
+    const int e = 2 * threadIdx.x, row = e / dec::W, col = n0 + e % dec::W;
+    uint32_t bw = 0u, rw = 0u;
+    if (LAST >= OP_BIAS) bw = *reinterpret_cast<const uint32_t *>(bias + col);
+    if (LAST >= OP_RES && row < M) rw = *reinterpret_cast<const uint32_t *>(R + (int64_t)row * N + col);
+
+    // A fragments (16x16x32 A operand: row i, k = 8g .. 8g+7 of each k-step);
+    // rows past M repeat row M-1 and are never stored.
     f16x8 afr[dec::MAXSTEPS];
     const uint16_t *arow = A + (int64_t)min(i, M - 1) * K + kbase + 8 * g;
 #pragma unroll
-    for (int t = 0; t < dec::MAXSTEPS; ++t) {
-        const uint16_t *src = arow + min(t, nsteps - 1) * dec::KSTEP;
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(afr[t]) : "v"(src));
+    for (int t = 0; t < dec::MAXSTEPS; ++t)
+        afr[t] = *reinterpret_cast<const f16x8 *>(arow + min(t, nsteps - 1) * dec::KSTEP);
+    // B slab: each instruction moves 8 k-rows (1 KiB); lane l lands at byte
+    // 16 l, i.e. row l / 8, unit l % 8, so it fetches the unit that the
+    // swizzle places there.
+    {
+        const int r = lane >> 3;
+        for (int blk = 0; blk < kw / 8; ++blk) {
+            const int k = blk * 8 + r;
+            const int u = (lane & 7) ^ dec_swz(k);
+            __builtin_amdgcn_global_load_lds(
+                (const FC_GLB void *)(B + (int64_t)(kbase + k) * N + n0 + u * 8),
+                (FC_LDS void *)(slab + blk * 1024), 16, 0, 0);
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0xF70);                            // vmcnt(0): slab and A landed
 
-    uint32_t b_off[2];
+    f32x4 acc[4];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int k = 8 * g + 4 * hh + (i >> 2);
-        b_off[hh] = (uint32_t)((k ^ (4 * ((k >> 3) & 1))) * 32 + (i & 3) * 8);
-    }
-#pragma unroll
-    for (int s = 0; s < dec::S - 1; ++s)
-        dec_issue_b(B, N, n0, kbase + min(s, nsteps - 1) * dec::KSTEP, ring + s * dec::STAGE);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < dec::MAXSTEPS; ++t) {
         if (t < nsteps) {
-            dec_issue_b(B, N, n0, kbase + min(t + dec::S - 1, nsteps - 1) * dec::KSTEP,
-                        ring + ((t + dec::S - 1) % dec::S) * dec::STAGE);
-            asm volatile("s_waitcnt vmcnt(15)" : "+v"(afr[t]));   // stage t (and every A load) landed
-            const uint32_t st = ring0 + (t % dec::S) * dec::STAGE;
-            u32x2 b0 = lds_read_tr16(st + b_off[0]);
-            u32x2 b1 = lds_read_tr16(st + b_off[1]);
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b0), "+v"(b1));
-            const u32x4 bw = {b0.x, b0.y, b1.x, b1.y};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[t], __builtin_bit_cast(f16x8, bw), acc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // lane i of group g addresses k-row 32t + 8g + 4hh + i/4,
+                // columns 16j + 4(i%4) .. +3; the transposing read hands
+                // lane i column 16j + i at four consecutive k
+                u32x2 bh[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = dec::KSTEP * t + 8 * g + 4 * hh + (i >> 2);
+                    bh[hh] = lds_read_tr16(slab0 + k * dec::ROW +
+                                           16 * ((2 * j + ((i & 3) >> 1)) ^ dec_swz(k)) + (i & 1) * 8);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bh[0]), "+v"(bh[1]));
+                const u32x4 bw = {bh[0].x, bh[0].y, bh[1].x, bh[1].y};
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[t], __builtin_bit_cast(f16x8, bw), acc[j],
+                                                                0, 0, 0);
+            }
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xF70);           // drain the clamped prefetches
-    __syncthreads();                             // every wave done with its ring
-    // 16x16 result layout: lane holds column (lane % 16), rows 4*(lane/16) + r
-    float *part = (float *)lds_raw;
+    __syncthreads();                                              // every wave done with its slab
+    // 16x16 result layout: lane holds column 16j + i, rows 4g + r
+    float *part = (float *)dec_lds;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[wave * 256 + (4 * g + r) * 16 + i] = acc[r];
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[wave * dec::TILE + (4 * g + r) * dec::W + 16 * j + i] = acc[j][r];
     __syncthreads();
-    if (threadIdx.x < 256) {
-        const int e = threadIdx.x, row = e >> 4, col = n0 + (e & 15);
-        float v = 0.0f;
+
+    // each thread owns the output pair e, e+1 of the 16x64 strip tile
+    float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
-        for (int w = 0; w < dec::WAVES; ++w) v += part[w * 256 + e];
-        if (row < M) {
-            const int64_t o = (int64_t)row * N + col;
-            const float bv = (LAST >= OP_BIAS) ? h2f(bias[col]) : 0.0f;
-            const float rv = (LAST >= OP_RES) ? h2f(R[o]) : 0.0f;
-            out[o] = f2h(apply_ops<OP_BIAS, LAST>(v, bv, rv));
-        }
+    for (int w = 0; w < dec::WAVES; ++w) {
+        const float2 pv = *reinterpret_cast<const float2 *>(part + w * dec::TILE + e);
+        v0 += pv.x;
+        v1 += pv.y;
     }
+    if (P == 1) {
+        if (row < M) dec_store_pair<LAST>(out, N, row, col, bw, rw, v0, v1);
+        return;
+    }
+    uint64_t *mine = reinterpret_cast<uint64_t *>(partials + ((int64_t)strip * P + split) * dec::TILE + e);
+    __hip_atomic_store(mine, __builtin_bit_cast(uint64_t, make_float2(v0, v1)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0xF70);                            // vmcnt(0): the partial is at the coherence point
+    __syncthreads();
+    if (threadIdx.x == 0)
+        is_last = __hip_atomic_fetch_add(counters + strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(P - 1);
+    __syncthreads();
+    if (!is_last) return;
+    // the P partials, eight loads in flight at a time, summed in split order
+    float s0 = 0.0f, s1 = 0.0f;
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(partials + (int64_t)strip * P * dec::TILE + e);
+    for (int p0 = 0; p0 < P; p0 += 8) {
+        uint64_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (p0 + q < P)
+                w[q] = __hip_atomic_load(src + (int64_t)(p0 + q) * (dec::TILE / 2), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (p0 + q < P) {
+                const float2 pv = __builtin_bit_cast(float2, w[q]);
+                s0 += pv.x;
+                s1 += pv.y;
+            }
+    }
+    if (row < M) dec_store_pair<LAST>(out, N, row, col, bw, rw, s0, s1);
+    if (threadIdx.x == 0) __hip_atomic_store(counters + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split of K for the decode kernel: the smallest power of two P with at least
+// 512 workgroups (strips x P: two per CU, which streams B faster than one
+// workgroup per CU with twice the loads in flight per wave), each wave
+// holding 1..4 k-steps; else the largest P that fits.  0 when the shape does
+// not fit (then the skinny kernel runs).
+static int decode_splits(int M, int N, int K)
+{
+    if (M > 16 || N % dec::W != 0 || K % (dec::WAVES * dec::KSTEP) != 0) return 0;
+    const int strips = N / dec::W;
+    int best = 0;
+    for (int P = 1; P <= dec::MAXP; P *= 2) {
+        if (K % (P * dec::WAVES * dec::KSTEP) != 0) break;
+        if (K > P * dec::WAVES * dec::KSTEP * dec::MAXSTEPS) continue;
+        best = P;
+        if ((int64_t)strips * P >= 512) break;
+    }
+    return best;
+}
+
+// Workspace bytes the decode kernel needs: arrival counters (256-byte
+// rounded) followed by fp32 partials; 0 when P <= 1.
+static size_t decode_scratch_bytes(int M, int N, int K)
+{
+    const int P = decode_splits(M, N, K);
+    if (P <= 1) return 0;
+    const size_t strips = (size_t)(N / dec::W);
+    return ((strips * 4 + 255) & ~(size_t)255) + strips * (size_t)P * dec::TILE * 4;
 }
 
 // ------------------------------------------------------------------ pointwise segments
@@ -918,13 +1024,26 @@ static int launch_gemm_cfg(const uint16_t *A, const uint16_t *B, const uint16_t 
     return launch_status();
 }
 
+// Scratch for the decode kernel inside the caller's workspace.
+struct DecodeScratch {
+    uint32_t *counters;
+    float *partials;
+};
+
 template <int LAST>
 static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
-                       uint16_t *out, int M, int N, int K, hipStream_t s)
+                       uint16_t *out, int M, int N, int K, DecodeScratch ds, hipStream_t s)
 {
-    if (M <= 16 && K % (dec::WAVES * dec::KSTEP) == 0 && K <= dec::WAVES * dec::KSTEP * dec::MAXSTEPS &&
-        N % 16 == 0) {
-        gemm_decode_kernel<LAST><<<N / 16, dec::NT, 0, s>>>(A, B, bias, R, out, M, N, K);
+    const int P = decode_splits(M, N, K);
+    if (P > 0) {
+        // dynamic LDS above 64 KiB has to be allowed per kernel
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void *)gemm_decode_kernel<LAST>, hipFuncAttributeMaxDynamicSharedMemorySize, dec::MAX_LDS);
+        if (attr != hipSuccess) return FC_ERR_HIP;
+        const int grid = (N / dec::W) * P;
+        const int lds = (K / P) * dec::ROW;
+        gemm_decode_kernel<LAST><<<grid, dec::NT, lds, s>>>(A, B, bias, R, out, M, N, K, P, ds.counters,
+                                                            ds.partials);
         return launch_status();
     }
     if (M <= 16) {
@@ -954,13 +1073,14 @@ static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bia
 }
 
 static int launch_gemm_segment(int last, const uint16_t *A, const uint16_t *B, const uint16_t *bias,
-                               const uint16_t *R, uint16_t *out, int M, int N, int K, hipStream_t s)
+                               const uint16_t *R, uint16_t *out, int M, int N, int K, DecodeScratch ds,
+                               hipStream_t s)
 {
     switch (last) {
-    case 0: return launch_gemm<0>(A, B, bias, R, out, M, N, K, s);
-    case 1: return launch_gemm<1>(A, B, bias, R, out, M, N, K, s);
-    case 2: return launch_gemm<2>(A, B, bias, R, out, M, N, K, s);
-    case 3: return launch_gemm<3>(A, B, bias, R, out, M, N, K, s);
+    case 0: return launch_gemm<0>(A, B, bias, R, out, M, N, K, ds, s);
+    case 1: return launch_gemm<1>(A, B, bias, R, out, M, N, K, ds, s);
+    case 2: return launch_gemm<2>(A, B, bias, R, out, M, N, K, ds, s);
+    case 3: return launch_gemm<3>(A, B, bias, R, out, M, N, K, ds, s);
     default: return FC_ERR_PLAN;
     }
 }
@@ -1007,11 +1127,19 @@ static bool plan_valid(const int *plan, int plan_len)
 
 using namespace fc;
 
+// Workspace layout: [decode counters + partials, when the shape takes the
+// split-K decode kernel][fp16 intermediate, 2MN bytes rounded up to 256, when
+// the plan has a cut].  The counters sit at offset 0 for every plan of a
+// shape, so one workspace serves all plans of that shape.
+static size_t inter_bytes(int M, int N, int plan_len)
+{
+    return plan_len > 1 ? ((2 * (size_t)M * (size_t)N + 255) & ~(size_t)255) : 0;
+}
+
 extern "C" size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_len)
 {
-    (void)K;
-    if (!plan_valid(plan, plan_len) || M < 1 || N < 1) return 0;
-    return plan_len > 1 ? 2 * (size_t)M * (size_t)N : 0;
+    if (!plan_valid(plan, plan_len) || M < 1 || N < 1 || K < 1) return 0;
+    return inter_bytes(M, N, plan_len) + decode_scratch_bytes(M, N, K);
 }
 
 extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
@@ -1030,14 +1158,22 @@ extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint
         overlaps(Y, mn, bias, (size_t)N * 2) || overlaps(Y, mn, R, mn))
         return FC_ERR_ALIAS;
     const size_t need = fc_gemm_workspace_bytes(M, N, K, plan, plan_len);
-    uint16_t *ws = static_cast<uint16_t *>(workspace);
+    const size_t dsb = decode_scratch_bytes(M, N, K);
+    uint16_t *ws = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + dsb);
+    DecodeScratch ds = {nullptr, nullptr};
     if (need) {
         if (!workspace || ws_bytes < need) return FC_ERR_WORKSPACE;
         if (!aligned16(workspace)) return FC_ERR_ALIGN;
-        if (overlaps(ws, need, A, (size_t)M * K * 2) || overlaps(ws, need, B, (size_t)K * N * 2) ||
-            overlaps(ws, need, bias, (size_t)N * 2) || overlaps(ws, need, R, mn) ||
-            overlaps(ws, need, Y, mn))
+        if (overlaps(workspace, need, A, (size_t)M * K * 2) || overlaps(workspace, need, B, (size_t)K * N * 2) ||
+            overlaps(workspace, need, bias, (size_t)N * 2) || overlaps(workspace, need, R, mn) ||
+            overlaps(workspace, need, Y, mn))
             return FC_ERR_ALIAS;
+        if (dsb) {
+            char *base = static_cast<char *>(workspace);
+            const size_t strips = (size_t)(N / dec::W);
+            ds.counters = reinterpret_cast<uint32_t *>(base);
+            ds.partials = reinterpret_cast<float *>(base + ((strips * 4 + 255) & ~(size_t)255));
+        }
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // operators: 0 = mm, 1 = bias, 2 = gelu, 3 = residual
@@ -1047,7 +1183,7 @@ extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint
         uint16_t *dst = (seg == plan_len - 1) ? Y : ws;
         int rc;
         if (seg == 0)
-            rc = launch_gemm_segment(last, A, B, bias, R, dst, M, N, K, s);
+            rc = launch_gemm_segment(last, A, B, bias, R, dst, M, N, K, ds, s);
         else
             rc = launch_pointwise(first, last, ws, bias, R, dst, (int64_t)M * N, N, s);
         if (rc != FC_OK) return rc;

@@ -99,17 +99,39 @@ size_t fc_chain_scratch_floats(int64_t n, int K, int mode, int fat_temps);
  *        reads it back.  Arithmetic is fp32 between cuts; Y is rounded to fp16
  *        (round to nearest even).
  *  workspace  device, >= fc_gemm_workspace_bytes() bytes, 16-byte aligned
- *        (NULL allowed when that is 0).  After a plan whose first segment is
- *        the bare GEMM, the workspace holds C = A.B as fp16 until the next
- *        segment overwrites it in place.
+ *        (NULL allowed when that is 0), not overlapping any operand.  Layout:
+ *        first, for shapes with M <= 16 that take the split-K decode kernel,
+ *        per-strip arrival counters and fp32 partial sums (D bytes, where
+ *        D = fc_gemm_workspace_bytes(M, N, K, {4}, 1)); then, when the plan
+ *        has a cut, the fp16 intermediate (round_up(2*M*N, 256) bytes at byte
+ *        offset D): after a plan whose first segment is the bare GEMM it holds
+ *        C = A.B until the next segment overwrites it in place.  The counters
+ *        must be zero when a call starts: hand in a zero-filled workspace the
+ *        first time; every call that completes leaves them zero again, so one
+ *        workspace serves any number of calls of one (M, N, K), under any
+ *        plan, without clearing.  Clear it again after using it for anything
+ *        else (another shape, other data).  Calls that overlap in time
+ *        (different streams) must not share a workspace.
+ *
+ *  Returns FC_OK, or FC_ERR_PLAN / FC_ERR_SHAPE / FC_ERR_UNSUPPORTED (N or
+ *  K not a multiple of 8) / FC_ERR_NULL / FC_ERR_ALIGN / FC_ERR_ALIAS /
+ *  FC_ERR_WORKSPACE (missing or too small) before anything is launched, or
+ *  FC_ERR_HIP if a launch fails.  The caller owns every buffer; the call is
+ *  asynchronous on `stream`.
  */
 int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
                      const uint16_t *R, uint16_t *Y, int M, int N, int K,
                      const int *plan, int plan_len, void *workspace, size_t ws_bytes,
                      fc_stream stream);
 
-/* Bytes of workspace for a plan: 2*M*N when the plan has a cut, else 0;
- * 0 also for an invalid plan (fc_gemm_epilogue then returns FC_ERR_PLAN). */
+/* Bytes of workspace for (M, N, K, plan): D + round_up(2*M*N, 256) when the
+ * plan has a cut, else D, where D is nonzero only when M <= 16, N % 64 == 0
+ * and K splits into P > 1 parts for the decode kernel: then
+ * D = round_up(4*N/64, 256) + 64*N*P (counters, then a 16x64 fp32 partial
+ * per 64-column strip and part).  P is the smallest power of two up to 64
+ * with 256*P dividing K, K <= 1024*P and (N/64)*P >= 512, else the largest
+ * power of two meeting the first two conditions (none: no decode kernel).
+ * 0 for an invalid plan or shape (fc_gemm_epilogue then returns an error). */
 size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_len);
 
 /* ---------------------------------------------------- causal softmax */

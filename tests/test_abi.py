@@ -46,13 +46,49 @@ def test_plan_accounting_matches_ledger_and_page():
     for row in g["plans"]:
         assert fc.fc_plan_bytes(4096, 4096, 4096, row["plan"]) == row["bytes"]
         assert fc.fc_plan_launches(row["plan"]) == row["launches"]
-    for M, N, K in [(16, 4096, 4096), (1, 8, 8), (17, 40, 24), (4096, 4096, 4096), (300, 1000, 72)]:
+    for M, N, K in [(16, 4096, 4096), (1, 8, 8), (17, 40, 24), (4096, 4096, 4096), (300, 1000, 72),
+                    (1, 2048, 2048), (16, 64, 65536), (8, 640, 768), (3, 128, 256)]:
         for plan in ledger.compositions(4):
             assert fc.fc_plan_bytes(M, N, K, plan) == ledger.plan_bytes(M, N, K, plan)
             assert fc.fc_plan_bytes(M, N, K, plan, 4) == ledger.plan_bytes(M, N, K, plan, 4)
             assert fc.fc_plan_launches(plan) == ledger.plan_launches(plan) == len(plan)
             ws = fc.fc_gemm_workspace_bytes(M, N, K, plan)
-            assert ws == (2 * M * N if len(plan) > 1 else 0)
+            assert ws == (-(-2 * M * N // 256) * 256 if len(plan) > 1 else 0) + decode_scratch(M, N, K)
+
+
+def decode_scratch(M, N, K):
+    """Workspace the split-K decode kernel adds, per the header: for M <= 16,
+    N % 64 == 0, K % 256 == 0, P is the smallest power of two with at most 4
+    32-deep k-steps per wave (K <= 1024 P) that gives N/64 * P >= 512
+    workgroups (else the largest such P, up to 64, with 256 P dividing K)."""
+    if M > 16 or N % 64 or K % 256:
+        return 0
+    strips, best, P = N // 64, 0, 1
+    while P <= 64 and K % (256 * P) == 0:
+        if K <= 1024 * P:
+            best = P
+            if strips * P >= 512:
+                break
+        P *= 2
+    if best <= 1:
+        return 0
+    return -(-4 * strips // 256) * 256 + strips * best * 16 * 64 * 4
+
+
+def test_decode_workspace_examples():
+    # 16x4096x4096: 64 strips x 8 splits = 512 workgroups
+    assert fc.fc_gemm_workspace_bytes(16, 4096, 4096, [4]) == 256 + 64 * 8 * 4096
+    assert fc.fc_gemm_workspace_bytes(16, 4096, 4096, [1, 3]) == 256 + 64 * 8 * 4096 + 131072
+    # 1x2048x2048: 32 strips x 8 splits (256 P must divide K)
+    assert fc.fc_gemm_workspace_bytes(1, 2048, 2048, [4]) == 256 + 32 * 8 * 4096
+    # N = 16384, K = 1024: 256 strips x 2 splits
+    assert fc.fc_gemm_workspace_bytes(16, 16384, 1024, [4]) == 1024 + 256 * 2 * 4096
+    # N = 32768: 512 strips fill the chip unsplit, no scratch
+    assert fc.fc_gemm_workspace_bytes(16, 32768, 1024, [4]) == 0
+    # shapes the decode kernel does not take
+    assert fc.fc_gemm_workspace_bytes(17, 4096, 4096, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(16, 4104, 4096, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(16, 4096, 4104, [4]) == 0
 
 
 @pytest.mark.parametrize("plan", [[], [0, 4], [5], [1, 1, 1], [2, -1, 3], [1, 1, 1, 1, 0]])

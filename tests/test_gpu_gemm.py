@@ -45,11 +45,15 @@ class Dev:
     def run(self, plan, keep_ws=False):
         Y = torch.empty((self.M, self.N), dtype=torch.float16, device="cuda")
         wsb = fc.fc_gemm_workspace_bytes(self.M, self.N, self.K, plan)
-        ws = torch.empty(max(wsb // 2, 1), dtype=torch.float16, device="cuda") if wsb else None
+        # zero-filled: the decode kernel's arrival counters live here
+        ws = torch.zeros(max(wsb // 2, 1), dtype=torch.float16, device="cuda") if wsb else None
         fc.fc_gemm_epilogue(self.A, self.B, self.bias, self.R, Y, plan, ws)
         torch.cuda.synchronize()
         if keep_ws:
-            return bits(Y), (bits(ws)[: self.M * self.N].reshape(self.M, self.N) if ws is not None else None)
+            # the intermediate follows the decode scratch, whose size is plan [4]'s workspace
+            off = fc.fc_gemm_workspace_bytes(self.M, self.N, self.K, [4]) // 2
+            return bits(Y), (bits(ws)[off: off + self.M * self.N].reshape(self.M, self.N)
+                             if ws is not None else None)
         return bits(Y)
 
 
@@ -168,3 +172,68 @@ def test_gelu_epilogue_accuracy(M, N, K):
         Y = d.run(plan).view(np.float16).astype(np.float64)
         assert np.all(Y == Y[0]), plan
         assert np.all(np.abs(Y[0] - ref) <= ulp + 1e-12), (plan, float(np.max(np.abs(Y[0] - ref) / ulp)))
+
+
+# M <= 16 shapes of the split-K decode kernel: no split (one or a few
+# workgroups, or 512 strips), 1-, 2- and 4-step waves, P = 2, 4, 8, 16 and 64.
+DECODE_SHAPES = [(1, 64, 256), (5, 640, 768), (16, 4096, 1024), (16, 4096, 8192), (1, 2048, 2048),
+                 (16, 64, 65536), (7, 16384, 512), (3, 32768, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
+def test_decode_kernel_shapes_all_plans(M, N, K):
+    announce(f"gemm decode path M={M} N={N} K={K} all plans")
+    d = Dev(M, N, K, salt=7 * M + N + K)
+    ref = oracle.gemm_epilogue_f64(*d.h)
+    for plan in ALL_PLANS:
+        ok, worst = tol_ok(d.run(plan), ref)
+        assert ok, (plan, worst)
+
+
+@pytest.mark.parametrize("plan", [[4], [1, 3]])
+def test_decode_workspace_reuse(plan):
+    """One zero-filled workspace for twelve back-to-back calls on two input
+    sets: every result matches the oracle and is bit-identical to the first
+    result of its set (the split partials are summed in a fixed order and no
+    stale partial from the previous call is read), and the arrival counters
+    are zero again afterwards."""
+    M, N, K = 16, 4096, 4096
+    announce(f"gemm decode workspace reuse plan={plan}")
+    sets = [Dev(M, N, K, salt=21), Dev(M, N, K, salt=22)]
+    refs = [oracle.gemm_epilogue_f64(*d.h) for d in sets]
+    wsb = fc.fc_gemm_workspace_bytes(M, N, K, plan)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    Ys = []
+    for it in range(12):
+        d = sets[it % 2]
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fc.fc_gemm_epilogue(d.A, d.B, d.bias, d.R, Y, plan, ws)
+        Ys.append(Y)
+    torch.cuda.synchronize()
+    outs = [bits(Y) for Y in Ys]
+    for it, y in enumerate(outs):
+        ok, worst = tol_ok(y, refs[it % 2])
+        assert ok, (it, worst)
+        assert np.array_equal(y, outs[it % 2]), it
+    counters = ws[: 4 * (N // 64)].cpu().numpy().view(np.uint32)
+    assert not counters.any()
+
+
+def test_decode_workspace_shared_by_plans():
+    """All eight plans in turn on one workspace (the counters sit at offset 0
+    for every plan of a shape), twice over."""
+    M, N, K = 16, 2048, 2048
+    announce("gemm decode one workspace for all plans")
+    d = Dev(M, N, K, salt=23)
+    ref = oracle.gemm_epilogue_f64(*d.h)
+    wsb = max(fc.fc_gemm_workspace_bytes(M, N, K, p) for p in ALL_PLANS)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    Ys = []
+    for plan in ALL_PLANS + ALL_PLANS:
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fc.fc_gemm_epilogue(d.A, d.B, d.bias, d.R, Y, plan, ws)
+        Ys.append((plan, Y))
+    torch.cuda.synchronize()
+    for plan, Y in Ys:
+        ok, worst = tol_ok(bits(Y), ref)
+        assert ok, (plan, worst)
