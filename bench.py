@@ -45,7 +45,7 @@ FAT_K, FAT_T = 4, 48
 AFFINE_N, AFFINE_K = 1048576, 8
 AFFINE_SETS = 40                    # 40 x 8 MiB touched per rotation (beyond the MALL)
 DECODE_MNK = (16, 4096, 4096)
-DECODE_SETS = 9                     # 9 copies of the 32 MiB weight matrix per rotation
+DECODE_SETS = 17                    # 17 copies of the 32 MiB weight matrix: ceil(512 MiB / footprint) + 1
 GEMM_MNK = (4096, 4096, 4096)
 PLANS = [[1, 1, 1, 1], [1, 3], [2, 2], [4]]
 SM_B, SM_H, SM_S = 8, 16, 2048
@@ -181,6 +181,108 @@ def cpu_baseline(budget_s=12.0):
     }
 
 
+def _median_ms(torch, stream, fn, reps, iters=7):
+    """Median over `iters` event pairs of the time per call of `reps` calls."""
+    ts = []
+    for _ in range(iters):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            fn(r)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / reps)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def measure_references(torch, stream, groups, bufs, fc):
+    """Reachable reference rates for each row's traffic mix on this device
+    (libfcenv.so probes: plain streams and a plain MFMA loop), on the rows' own
+    cold buffers.  A fraction of 1 or more means the kernel moves its bytes at
+    least as fast as a plain stream of the same mix."""
+    from gemm_epilogues_amd import envelope as env
+    C = env.fce_chunk_bytes()
+    dev = torch.device("cuda", 0)
+    out = {}
+    for _ in range(2):                         # first pass warms the probes up
+        if "chain" in groups:
+            sets, _ = bufs["chain"]
+            nb = CHAIN_N * 4
+            ms = _median_ms(torch, stream, lambda r: env.fce_mix(sets[r][0], nb, sets[r][1], nb), CHAIN_SETS)
+            out["copy_64MiB_cold"] = {"GBps": round(2 * nb / ms / 1e6, 1), "bytes": 2 * nb,
+                                      "probe": "fce_mix read 64 MiB + write 64 MiB, 5 rotating sets"}
+        if "softmax" in groups:
+            sd, so = bufs["softmax"]
+            W = sd.numel() * 2
+            for tile in (64, 2048):
+                rb = fc.fc_softmax_bytes(SM_B * SM_H, SM_S, tile, fc.FC_SOFTMAX_FUSED) - W
+                rb -= rb % C
+                ms = _median_ms(torch, stream, lambda r, rb=rb: env.fce_mix(sd, rb, so, W), 1)
+                out[f"mix_softmax_T{tile}"] = {"GBps": round((rb + W) / ms / 1e6, 1), "read_bytes": rb,
+                                               "write_bytes": W,
+                                               "probe": "fce_mix with the row's read/write byte mix"}
+        if "decode" in groups:
+            dsets = bufs["decode"]
+            nb = dsets[0][1].numel() * 2
+            sink = torch.zeros(1, dtype=torch.float32, device=dev)
+            ms = _median_ms(torch, stream, lambda r: env.fce_read(dsets[r][1], nb, sink), DECODE_SETS)
+            out["read_32MiB_cold"] = {"GBps": round(nb / ms / 1e6, 1), "bytes": nb,
+                                      "probe": f"fce_read of B, {DECODE_SETS} rotating copies"}
+        if "gemm" in groups:
+            msink = torch.empty(env.fce_mfma_sink_floats(), dtype=torch.float32, device=dev)
+            iters = 2000
+            ms = _median_ms(torch, stream, lambda r: env.fce_mfma(msink, iters), 1)
+            out["mfma_f16_random"] = {"TFLOPs": round(env.fce_mfma_flops(iters) / ms / 1e9, 1),
+                                      "probe": "fce_mfma: v_mfma_f32_32x32x16_f16 on changing random operands"}
+    return out
+
+
+def measure_torch_rows(torch, stream, groups, bufs):
+    """The same work as PyTorch eager ops (one library kernel per operator,
+    intermediates through HBM): the unfused baseline a user would otherwise
+    run.  Times in us per call."""
+    F = torch.nn.functional
+    out = {}
+    if "chain" in groups:
+        sets, coef = bufs["chain"]
+        a, b = coef[8]
+        al, bl = [float(v) for v in a], [float(v) for v in b]
+
+        def chain(r):
+            y = sets[r][0]
+            for st in range(8):
+                y = y * al[st] + bl[st]
+                if st % 2 == 0:
+                    y = torch.relu(y)
+            return y
+        out["chain_K8_us"] = round(_median_ms(torch, stream, chain, CHAIN_SETS) * 1e3, 2)
+    if "decode" in groups:
+        dsets = bufs["decode"]
+        out["decode_us"] = round(_median_ms(
+            torch, stream, lambda r: F.gelu(torch.addmm(dsets[r][2], dsets[r][0], dsets[r][1])) + dsets[r][3],
+            DECODE_SETS) * 1e3, 2)
+        out["decode_matmul_only_us"] = round(_median_ms(
+            torch, stream, lambda r: torch.matmul(dsets[r][0], dsets[r][1]), DECODE_SETS) * 1e3, 2)
+    if "gemm" in groups:
+        A, B, bias, R = bufs["gemm"]
+        out["gemm_4096_us"] = round(_median_ms(
+            torch, stream, lambda r: F.gelu(torch.addmm(bias, A, B)) + R, 1, iters=11) * 1e3, 2)
+        out["gemm_4096_matmul_only_us"] = round(_median_ms(
+            torch, stream, lambda r: torch.matmul(A, B), 1, iters=11) * 1e3, 2)
+    if "softmax" in groups:
+        sd, _ = bufs["softmax"]
+        S = sd.shape[-1]
+        mask = torch.ones((S, S), dtype=torch.bool, device=sd.device).triu(1)
+
+        def sm(r):
+            return torch.softmax((sd.float() * SCALE).masked_fill(mask, float("-inf")), -1).to(torch.bfloat16)
+        out["softmax_us"] = round(_median_ms(torch, stream, sm, 1, iters=3) * 1e3, 2)
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +294,10 @@ def main():
                          "kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--rows", default="chain,affine,decode,gemm,softmax",
                     help="comma list of row groups to run (default: all)")
+    ap.add_argument("--no-references", action="store_true",
+                    help="skip the stream/MFMA reference probes (libfcenv.so) timed after the steps")
+    ap.add_argument("--no-torch-rows", action="store_true",
+                    help="skip the PyTorch eager (unfused library) rows timed after the steps")
     ap.add_argument("--graph", action="store_true",
                     help="time each row as one replay of a HIP graph captured from its calls")
     args = ap.parse_args()
@@ -218,6 +324,7 @@ def main():
     # ---------------------------------------------------------------- inputs (resident in HBM)
     steps = []                      # callables(timer) making up one step
     comp = {}
+    bufs = {}                       # device inputs, for the reference probes and the torch rows
 
     if "chain" in groups:
         log("inputs: chain")
@@ -229,6 +336,7 @@ def main():
         coef = {K: synth.chain_inputs(1, K)[1:] for K in CHAIN_KS}
         sink = torch.empty(fc.fc_chain_scratch_floats(CHAIN_N, FAT_K, fc.FC_CHAIN_FAT, FAT_T),
                            dtype=torch.float32, device=dev)
+        bufs["chain"] = (sets, coef)
 
         def chain_rows(tm, step_i):
             for K in CHAIN_KS:
@@ -239,6 +347,9 @@ def main():
                 tm(f"chain_naive_K{K}",
                    lambda r, a=a, b=b: fc.fc_chain(sets[r][0], sets[r][1], a, b, True,
                                                    fc.FC_CHAIN_NAIVE, sets[r][2]), reps=CHAIN_SETS)
+            a, b = coef[8]
+            tm("chain_fused_K8_warm",
+               lambda r: fc.fc_chain(sets[0][0], sets[0][1], a, b, True, fc.FC_CHAIN_FUSED), reps=CHAIN_SETS)
             a, b = coef[FAT_K]
             tm(f"chain_fat_K{FAT_K}_T{FAT_T}",
                lambda r: fc.fc_chain(sets[r][0], sets[r][1], a, b, True, fc.FC_CHAIN_FAT, sink, FAT_T),
@@ -273,11 +384,15 @@ def main():
             dsets.append(tdv + [torch.empty((M, N), dtype=torch.float16, device=dev),
                                 torch.zeros(wsb, dtype=torch.uint8, device=dev)])
 
+        bufs["decode"] = dsets
+
         def decode_rows(tm, step_i):
             for plan in PLANS:
                 name = "decode_plan" + "".join(map(str, plan))
                 tm(name, lambda r, plan=plan: fc.fc_gemm_epilogue(*dsets[r][:5], plan, dsets[r][5]),
                    reps=DECODE_SETS)
+            tm("decode_plan4_warm", lambda r: fc.fc_gemm_epilogue(*dsets[0][:5], [4], dsets[0][5]),
+               reps=DECODE_SETS)
         steps.append(decode_rows)
 
     if "gemm" in groups:
@@ -286,6 +401,7 @@ def main():
         A, B, bias, R = synth.gemm_inputs(M, N, K)
         td = [torch.from_numpy(v.view(np.int16)).to(dev).view(torch.float16) for v in (A, B, bias, R)]
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        bufs["gemm"] = td
         ws = torch.zeros(max(fc.fc_gemm_workspace_bytes(M, N, K, p) for p in PLANS), dtype=torch.uint8,
                          device=dev)
 
@@ -303,6 +419,7 @@ def main():
         sd = torch.from_numpy(s.view(np.int16)).to(dev).view(torch.bfloat16)
         del s
         out = torch.empty_like(sd)
+        bufs["softmax"] = (sd, out)
         wsb = fc.fc_softmax_workspace_bytes(BH, S, fc.FC_SOFTMAX_UNFUSED)
         smws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
@@ -345,6 +462,8 @@ def main():
     tm.collect()
     ms_per_step = wall / max(args.steps, 1) * 1e3
     log(f"timed region {wall:.3f}s, {ms_per_step:.3f} ms/step")
+    refs = {} if args.no_references else measure_references(torch, stream, groups, bufs, fc)
+    torch_rows = {} if args.no_torch_rows else measure_torch_rows(torch, stream, groups, bufs)
 
     # ---------------------------------------------------------------- derived numbers
     fused_bytes = 0
@@ -366,6 +485,7 @@ def main():
             }
             fused_bytes += bf
             fused_ms += tf
+        comp["chain_K8"]["fused_warm_us"] = round(tm.median("chain_fused_K8_warm") * 1e3, 2)
         tfat = tm.median(f"chain_fat_K{FAT_K}_T{FAT_T}")
         comp[f"chain_fat_K{FAT_K}_T{FAT_T}"] = {
             "us": round(tfat * 1e3, 2),
@@ -388,6 +508,7 @@ def main():
             comp[name] = {"us": round(t_ * 1e3, 2), "bytes": b, "GBps": round(b / (t_ * 1e-3) / 1e9, 1),
                           "frac_hbm": round(b / (t_ * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "launches": fc.fc_plan_launches(plan)}
+        comp["decode_plan4"]["warm_us"] = round(tm.median("decode_plan4_warm") * 1e3, 2)
     if "softmax" in groups:
         BH, S = SM_B * SM_H, SM_S
         for tile in SM_TILES:
@@ -465,6 +586,32 @@ def main():
                        "traffic": load_traffic("decode_plan4",
                                                os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "gemm.hip"))})
 
+    def attach_reference(obj, key, field):
+        c = refs.get(key)
+        if obj is not None and c:
+            obj["reference"] = c[field]
+            obj["frac_of_reference"] = round(obj["achieved"] / c[field], 4)
+            obj["reference_probe"] = c["probe"]
+
+    attach_reference(roofline, "mix_softmax_T64", "GBps")
+    for o in others:
+        if o["kernel"].startswith("chain_fused"):
+            attach_reference(o, "copy_64MiB_cold", "GBps")
+        elif o["kernel"].startswith("gemm_ring"):
+            attach_reference(o, "mfma_f16_random", "TFLOPs")
+        elif o["kernel"].startswith("gemm_decode"):
+            attach_reference(o, "read_32MiB_cold", "GBps")
+    if "softmax_fused_T2048" in comp and "mix_softmax_T2048" in refs:
+        comp["softmax_fused_T2048"]["frac_of_reference"] = round(
+            comp["softmax_fused_T2048"]["GBps"] / refs["mix_softmax_T2048"]["GBps"], 4)
+    if torch_rows:
+        pairs = {"chain_K8_us": ("chain_K8", "fused_us"), "decode_us": ("decode_plan4", "us"),
+                 "gemm_4096_us": ("gemm_plan4", "us"), "softmax_us": ("softmax_fused_T64", "us")}
+        for k, (row, f) in pairs.items():
+            if k in torch_rows and row in comp:
+                torch_rows[k.replace("_us", "_speedup_fused_vs_torch")] = round(torch_rows[k] / comp[row][f], 2)
+        comp["torch_eager"] = torch_rows
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)")
@@ -496,6 +643,7 @@ def main():
         },
         "roofline": roofline,
         "rooflines_other": others,
+        "references": refs,
         "cpu_baseline": cpu,
         "components": comp,
     }

@@ -1,7 +1,8 @@
 """Build the fused-chain library: hipcc for gfx950 -> gemm_epilogues_amd/libfc.so.
 
 Every translation unit under csrc/ is compiled in parallel to an object file,
-then linked into one shared library exporting the C ABI of include/fc.h.  The
+then linked into one shared library exporting the C ABI of include/fc.h, and
+the measurement probes into libfcenv.so (include/fc_envelope.h).  The
 compiler's per-kernel resource report (VGPRs, AGPRs, SGPRs, LDS, scratch,
 occupancy) is parsed into kernel_resources.json next to the library.
 
@@ -20,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfc.so")
+ENV_LIB = os.path.join(HERE, "libfcenv.so")
 RES = os.path.join(HERE, "kernel_resources.json")
 
 ARCH = "gfx950"
@@ -29,6 +31,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]
 SOURCES = ["chain.hip", "chain_fat.hip", "softmax.hip", "gemm.hip", "api.cpp"]
+# measurement probes (stream and MFMA ceilings), a library of their own
+ENV_SOURCES = ["envelope.hip"]
 
 
 def _parse_resources(text: str) -> dict:
@@ -48,7 +52,7 @@ def _parse_resources(text: str) -> dict:
 def build(jobs: int = 0, verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     procs = []
-    for src in SOURCES:
+    for src in SOURCES + ENV_SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(OBJ, src + ".o")
         cmd = [HIPCC] + COMMON + ["-c", path, "-o", obj]
@@ -71,11 +75,12 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
         for src, err in failed:
             sys.stderr.write(f"--- {src} failed ---\n{err}\n")
         raise RuntimeError("hipcc failed: " + ", ".join(s for s, _ in failed))
-    tmp = LIB + ".tmp"
-    link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + \
-        [os.path.join(OBJ, s + ".o") for s in SOURCES]
-    subprocess.run(link, check=True)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (ENV_LIB, ENV_SOURCES)):
+        tmp = lib + ".tmp"
+        link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + \
+            [os.path.join(OBJ, s + ".o") for s in srcs]
+        subprocess.run(link, check=True)
+        os.replace(tmp, lib)
     with open(RES, "w") as f:
         json.dump(resources, f, indent=1, sort_keys=True)
     return LIB

@@ -652,17 +652,17 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 0, j), F[cb].a[0][i],
                                                                        acc[i][j], 0, 0, 0);
-            // slab tt+3 goes to the stage read for step tt-1, which every wave
-            // finished before the previous barrier; past the end a clamped
+            // slab tt+3 goes to the stage read for step tt-1: every wave read
+            // its fragments for step tt-1 during step tt-2 and waited for all
+            // of them before the barrier of step tt-1; past the end a clamped
             // re-read lands in a stage that is never read
             ring_issue(A, B, M, N, K, m0, n0, min(tt + ring::S - 1, nk - 1),
                        lds + ((tt + ring::S - 1) % ring::S) * ring::STAGE);
             __builtin_amdgcn_s_waitcnt(0xF78);   // vmcnt(8): slab tt+1 of this wave landed
-            __builtin_amdgcn_s_barrier();        // ... and of every wave
+            frag_wait1(F[cb]);                   // every fragment read of stage tt done
+            __builtin_amdgcn_s_barrier();        // ... in every wave, and slab tt+1 landed
             __builtin_amdgcn_sched_barrier(0);
             const uint32_t st = lds0 + ((tt + 1) % ring::S) * ring::STAGE;
-            frag_wait1(F[cb]);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int i = q >> 1, j = q & 1;

@@ -7,6 +7,7 @@ Every validation case below is invalid by construction, so no kernel is ever
 launched from this file (the pointers are fake host addresses).
 """
 import ctypes
+import os
 import re
 
 import pytest
@@ -215,3 +216,38 @@ def test_softmax_validation():
     assert L.fc_causal_mask_materialise(None, 1, 4, None) == fc.FC_ERR_NULL
     assert L.fc_causal_mask_materialise(MIS, 1, 4, None) == fc.FC_ERR_ALIGN
     assert L.fc_causal_mask_materialise(FAKE, 0, 4, None) == fc.FC_ERR_SHAPE
+
+
+# ---------------------------------------------------------------- measurement probes (libfcenv.so)
+
+def test_envelope_library_exports_its_header():
+    from gemm_epilogues_amd import envelope as env
+    text = open(os.path.join(os.path.dirname(fc.HEADER), "fc_envelope.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(fce_[a-z0-9_]+)\s*\(", text)))
+    lib = ctypes.CDLL(env.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(env.EXPORTED)
+    assert env.fce_chunk_bytes() == 32768
+    assert env.fce_mfma_sink_floats() == 1024 * 256
+    assert env.fce_mfma_flops(10) == 1024 * 4 * 10 * 8 * 2 * 32 * 32 * 16
+    assert env.fce_mfma_flops(0) == 0.0
+
+
+def test_envelope_validation_before_launch():
+    from gemm_epilogues_amd import envelope as env
+    L = env._lib
+    C = 32768
+    assert L.fce_mix(FAKE, C, None, C, None) == fc.FC_ERR_NULL
+    assert L.fce_mix(None, C, FAKE, C, None) == fc.FC_ERR_NULL
+    assert L.fce_mix(FAKE, 0, FAKE, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fce_mix(FAKE, C, FAKE + 4 * C, C + 16, None) == fc.FC_ERR_SHAPE
+    assert L.fce_mix(FAKE, 2 * C, FAKE + 4 * C, C, None) == fc.FC_ERR_SHAPE
+    assert L.fce_mix(MIS, C, FAKE + 4 * C, C, None) == fc.FC_ERR_ALIGN
+    assert L.fce_mix(FAKE, C, FAKE + C // 2, C, None) == fc.FC_ERR_ALIAS
+    assert L.fce_read(None, C, FAKE, None) == fc.FC_ERR_NULL
+    assert L.fce_read(FAKE, C + 1, FAKE, None) == fc.FC_ERR_SHAPE
+    assert L.fce_read(MIS, C, FAKE, None) == fc.FC_ERR_ALIGN
+    assert L.fce_mfma(None, 1, None) == fc.FC_ERR_NULL
+    assert L.fce_mfma(FAKE, 0, None) == fc.FC_ERR_SHAPE
