@@ -5,7 +5,8 @@ leg may import this package.  The product library (``gemm_epilogues_amd``)
 never imports it and shares no code with it.
 
 ``oracle.c`` holds the plain fp64 definitions (chain, GEMM + bias + GELU +
-residual, causal softmax); ``ledger.py`` the byte and launch ledgers.  This
+residual, causal softmax, causal attention); ``ledger.py`` the byte and launch
+ledgers.  This
 module builds ``oracle.c`` with gcc and wraps it with ctypes/numpy.
 
 Every function here is pinned by a CPU test against something other than
@@ -63,6 +64,8 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = None
+        lib.oracle_causal_attention_rows.argtypes = [P, P, P, I64, I64, D, P, I64, P]
+        lib.oracle_causal_attention_rows.restype = I
         for name, arg in (("oracle_gelu", D), ("oracle_half_to_double", ctypes.c_uint16),
                           ("oracle_bf16_to_double", ctypes.c_uint16)):
             fn = getattr(lib, name)
@@ -177,3 +180,27 @@ def causal_mask01(S: int) -> np.ndarray:
     i = np.arange(S)[:, None]
     j = np.arange(S)[None, :]
     return (j <= i).astype(np.float64)
+
+
+# ---------------------------------------------------------------- causal attention
+
+def causal_attention_rows(Q, K, V, scale: float, row_ids) -> np.ndarray:
+    """Rows r = bh*S + i of O = softmax(scale * Q K^T, causal) V in fp64, from
+    bf16 bits Q, K, V [BH, S, D]; shape [len(row_ids), D]."""
+    q, k, v = _c(Q, np.uint16), _c(K, np.uint16), _c(V, np.uint16)
+    assert q.shape == k.shape == v.shape and q.ndim == 3
+    BH, S, D = q.shape
+    rid = _c(row_ids, np.int64)
+    assert rid.size == 0 or (rid.min() >= 0 and rid.max() < BH * S)
+    out = np.empty((rid.size, D), dtype=np.float64)
+    rc = _load().oracle_causal_attention_rows(_p(q), _p(k), _p(v), S, D, float(scale), _p(rid),
+                                              rid.size, _p(out))
+    if rc != 0:
+        raise MemoryError("oracle_causal_attention_rows: allocation failed")
+    return out
+
+
+def causal_attention_f64(Q, K, V, scale: float) -> np.ndarray:
+    """All rows of O, shape [BH, S, D] (small inputs only)."""
+    BH, S, D = np.shape(Q)
+    return causal_attention_rows(Q, K, V, scale, np.arange(BH * S)).reshape(BH, S, D)

@@ -22,6 +22,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#include <stdlib.h>
 
 /* ------------------------------------------------------------ storage decode */
 
@@ -205,4 +206,69 @@ void oracle_causal_softmax_f64(const uint16_t *scores, int64_t BH, int64_t S,
     #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t r = 0; r < BH * S; ++r)
         softmax_row(scores + r * S, S, r % S, scale, out + r * S);
+}
+
+/* ------------------------------------------------------------ causal attention */
+
+/*
+ * Causal scaled dot-product attention, the chain the pages' score tensor sits
+ * in ("AIGC 基本功", section 3.5: query i sees keys j <= i; the attention-tail
+ * section: scale, mask, softmax; and its further-reading list, which names the
+ * online-softmax kernel that never materialises the scores as the way to
+ * remove that tensor).  Its result is plain attention, written out here:
+ *   z_j = scale * sum_d Q[i][d] K[j][d]          for j <= i
+ *   m = max_j z_j ; p_j = exp(z_j - m) ; l = sum_j p_j
+ *   O[i][d] = sum_j p_j V[j][d] / l
+ * Q, K, V: bf16 bits [BH, S, D] row-major; values decoded exactly to fp64.
+ */
+static void attention_row(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                          int64_t S, int64_t D, int64_t bh, int64_t i, double scale,
+                          double *z, double *orow)
+{
+    const uint16_t *q = Q + (bh * S + i) * D;
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+        const uint16_t *k = K + (bh * S + j) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += bf16_bits_to_double(q[d]) * bf16_bits_to_double(k[d]);
+        z[j] = scale * dot;
+        if (z[j] > m)
+            m = z[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        z[j] = exp(z[j] - m);
+        l += z[j];
+    }
+    for (int64_t d = 0; d < D; ++d)
+        orow[d] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        const uint16_t *v = V + (bh * S + j) * D;
+        for (int64_t d = 0; d < D; ++d)
+            orow[d] += z[j] * bf16_bits_to_double(v[d]);
+    }
+    for (int64_t d = 0; d < D; ++d)
+        orow[d] /= l;
+}
+
+/* Rows r = bh*S + i of O for the listed row ids; out: nrows x D doubles.
+ * Returns 0, or -1 if a row's score buffer cannot be allocated. */
+int oracle_causal_attention_rows(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                 int64_t S, int64_t D, double scale,
+                                 const int64_t *row_ids, int64_t nrows, double *out)
+{
+    int failed = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t t = 0; t < nrows; ++t) {
+        int64_t r = row_ids[t];
+        double *z = (double *)malloc((size_t)(r % S + 1) * sizeof(double));
+        if (!z) {
+            failed = 1;
+            continue;
+        }
+        attention_row(Q, K, V, S, D, r / S, r % S, scale, z, out + t * D);
+        free(z);
+    }
+    return failed ? -1 : 0;
 }

@@ -40,6 +40,9 @@ _ROLES = {
     "gemm.int.A": 9,
     "gemm.int.B": 10,
     "misc": 11,
+    "attn.Q": 12,
+    "attn.K": 13,
+    "attn.V": 14,
 }
 _N_ROLES = 32
 
@@ -129,3 +132,14 @@ def softmax_inputs(BH: int, S: int, salt: int = 0, chunk: int = 1 << 26) -> np.n
         v *= k
         out[lo:hi] = f32_to_bf16_bits(v)
     return out.reshape(BH, S, S)
+
+
+def attention_inputs(BH: int, S: int, D: int = 128, salt: int = 0):
+    """Q, K, V as bf16 bits [BH, S, D], each bf16(fp32(N(0,1))): with D = 128
+    and scale 1/sqrt(128) the scaled scores q.k have the N(0,1) spread of the
+    softmax workload's scores."""
+    out = []
+    for role in ("attn.Q", "attn.K", "attn.V"):
+        v = rng(role, salt).standard_normal(BH * S * D, dtype=np.float32)
+        out.append(f32_to_bf16_bits(v).reshape(BH, S, D))
+    return tuple(out)
