@@ -86,6 +86,9 @@ _SIGS = {
     "fc_plan_launches": (_I, [_P, _I]),
     "fc_chain_bytes": (_U64, [_I64, _I, _I]),
     "fc_softmax_bytes": (_U64, [_I64, _I, _I, _I]),
+    "fc_causal_attention": (_I, [_P, _P, _P, _P, _I64, _I, _I, _F, _P]),
+    "fc_attention_flops": (_U64, [_I64, _I, _I]),
+    "fc_attention_bytes": (_U64, [_I64, _I, _I]),
     "fc_status_string": (ctypes.c_char_p, [_I]),
     "fc_version": (ctypes.c_char_p, []),
 }
@@ -304,6 +307,30 @@ def fc_causal_mask_materialise(mask, BH: int, S: int, stream=None) -> None:
         del torch
     rc = _lib.fc_causal_mask_materialise(_ptr(mask), int(BH), int(S), _stream(stream))
     _check(rc, "fc_causal_mask_materialise")
+
+
+# ---------------------------------------------------------------- causal attention
+
+def fc_causal_attention(Q, K, V, O, scale: float, stream=None) -> None:
+    """O = causal softmax(scale * Q K^T) V; bf16 device tensors [BH, S, D] or [B, H, S, D]."""
+    torch = _torch()
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O")):
+        _dev(t, torch.bfloat16, nm)
+    if Q.dim() not in (3, 4) or not (Q.shape == K.shape == V.shape == O.shape):
+        raise ValueError("Q, K, V, O must share one [BH,S,D] or [B,H,S,D] shape")
+    S, D = Q.shape[-2], Q.shape[-1]
+    BH = Q.numel() // (S * D) if S * D else 0
+    rc = _lib.fc_causal_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), int(BH), int(S), int(D),
+                                  float(scale), _stream(stream))
+    _check(rc, "fc_causal_attention")
+
+
+def fc_attention_flops(BH: int, S: int, D: int) -> int:
+    return int(_lib.fc_attention_flops(int(BH), int(S), int(D)))
+
+
+def fc_attention_bytes(BH: int, S: int, D: int) -> int:
+    return int(_lib.fc_attention_bytes(int(BH), int(S), int(D)))
 
 
 # ---------------------------------------------------------------- accounting (host only)

@@ -1,0 +1,305 @@
+// Causal attention in one kernel that never writes the scores: per query tile,
+// key/value tiles stream through LDS and an online softmax keeps the running
+// row max and sum ("AIGC 基本功｜算子融合与 CUDA Graph-Fusion", section 3.5: causal
+// mask and block skipping; its further-reading list: the attention kernel
+// that removes the S x S score tensor by normalising as it goes).
+//
+// Layout: Q, K, V, O bf16 [BH, S, 128] row-major.  A workgroup owns 128
+// queries of one head (4 waves x 32); 64-key tiles of K and V are loaded
+// into a double-buffered LDS ring (2 x (16 + 16) KiB) with direct-to-LDS
+// loads, one tile ahead.  Per tile each wave computes
+//   S^T = K Q^T           (v_mfma_f32_32x32x16_bf16, K from LDS as the A
+//                          operand, Q fragments held in registers)
+// so a lane owns one query and 32 of the tile's 64 keys (the other 32 are in
+// lane +-32): the row max and sum need one cross-half swap
+// (v_permlane32_swap), the running rescale of the output stays in the lane.
+//   O^T += V^T P^T        (P packed to bf16 straight from the S registers as
+//                          the B operand; V^T fragments come from LDS with the
+//                          transposing read ds_read_b64_tr_b16 in the same key
+//                          order as the P registers)
+// The softmax runs in the log2 domain (scores pre-scaled by scale*log2 e,
+// v_exp_f32).  Key tiles entirely above a wave's queries are skipped; tiles
+// that cross its diagonal are masked per element.  Query tiles with the most
+// keys are dispatched first.
+//
+// LDS swizzles (16-byte units u of a 256-byte key row r):
+//   K: u ^ (r & 15)      -- the b128 fragment reads of 16 consecutive keys hit
+//                           16 different units
+//   V: u ^ 4 (r & 3)     -- the transposing reads of 4 consecutive keys x two
+//                           32-byte column pairs hit 8 different 32-byte slots
+#include "fc_internal.h"
+
+#define FC_LDS __attribute__((address_space(3)))
+#define FC_GLB __attribute__((address_space(1)))
+
+namespace fc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace att {
+constexpr int D = 128, BQ = 128, BKV = 64, WAVES = 4, NT = WAVES * 64;
+constexpr int ROWB = D * 2;                   // bytes per key row
+constexpr int TILE = BKV * ROWB;              // 16 KiB
+constexpr int STAGE = 2 * TILE;               // K tile, then V tile
+constexpr int LDS_BYTES = 2 * STAGE;          // two stages
+constexpr float LOG2E = 1.4426950408889634f;
+}
+
+__device__ __forceinline__ u32x4 att_read_b128(uint32_t addr)
+{
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ u32x2 att_read_tr16(uint32_t addr)
+{
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// This wave's quarter of key/value tile kt (rows clamped to S-1; such rows
+// only meet masked queries or queries past S) into stage st.
+__device__ __forceinline__ void att_issue(const uint16_t *__restrict__ Kh, const uint16_t *__restrict__ Vh,
+                                          int S, int kt, FC_LDS char *st)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int blk = wave * 4 + q;                       // 1 KiB = 4 key rows
+        const int r = blk * 4 + (lane >> 4);
+        const int64_t key = min(kt * att::BKV + r, S - 1);
+        __builtin_amdgcn_global_load_lds((const FC_GLB void *)(Kh + key * att::D + (p ^ (r & 15)) * 8),
+                                         (FC_LDS void *)(st + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const FC_GLB void *)(Vh + key * att::D + (p ^ (4 * (r & 3))) * 8),
+                                         (FC_LDS void *)(st + att::TILE + blk * 1024), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ float att_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max and sum over the two 32-lane halves: both halves end with the same value
+__device__ __forceinline__ float att_half_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float att_half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t att_pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+__global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    uint16_t *__restrict__ O, int64_t BH, int S, float scale_log2)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_raw[att::LDS_BYTES];
+    FC_LDS char *lds = (FC_LDS char *)lds_raw;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hl = lane >> 5, l32 = lane & 31;
+
+    // heaviest query tiles first: the first BH workgroups take the last tile of every head
+    const int nqt = (S + att::BQ - 1) / att::BQ;
+    const int64_t bh = blockIdx.x % BH;
+    const int qt = nqt - 1 - (int)(blockIdx.x / BH);
+    const int q0 = qt * att::BQ;
+    const uint16_t *Qh = Q + bh * (int64_t)S * att::D;
+    const uint16_t *Kh = K + bh * (int64_t)S * att::D;
+    const uint16_t *Vh = V + bh * (int64_t)S * att::D;
+
+    const int wq0 = q0 + wave * 32;                         // this wave's first query
+    const int query = wq0 + l32;                            // this lane's query
+    const int kt_last = min(q0 + att::BQ - 1, S - 1) / att::BKV;
+    const int wave_kt_last = min(wq0 + 31, S - 1) / att::BKV;
+
+    // Q fragments (B operand of S^T = K Q^T): query l32, d = 16 ks + 8 hl .. +7
+    u32x4 qf[8];
+    {
+        const uint16_t *qrow = Qh + (int64_t)min(query, S - 1) * att::D + 8 * hl;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + 16 * ks);
+    }
+
+    // per-lane LDS byte offsets (within a stage)
+    uint32_t koff[2][8];                                    // [key m-tile][k-step]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int r = 32 * t + l32;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) koff[t][ks] = r * att::ROWB + (((2 * ks + hl) ^ (r & 15)) * 16);
+    }
+    // V^T fragments: lane (group g = lane / 16, j = lane % 16) addresses key
+    // k0 + j/4, d = 32 mt + 16 (g & 1) + 4 (j % 4); k0 = 32 t + 16 h + 8 e2 + 4 hl
+    uint32_t voff_base[2];                                  // [e2], for t = h = mt = 0
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+        const int key = 8 * e2 + 4 * hl + (j >> 2);        // key & 3 == j >> 2 for every t, h
+        const int unit = (16 * (g & 1) + 4 * (j & 3)) / 8;  // + 4 mt
+        voff_base[e2] = att::TILE + key * att::ROWB + ((unit ^ (4 * (key & 3))) * 16) + (j & 1) * 8;
+    }
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    att_issue(Kh, Vh, S, 0, lds);
+    for (int kt = 0; kt <= kt_last; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0xF70);                  // vmcnt(0): this wave's share of tile kt landed
+        __builtin_amdgcn_s_barrier();                       // every wave's share landed; stage kt-1 is free
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt < kt_last) att_issue(Kh, Vh, S, kt + 1, lds + ((kt + 1) & 1) * att::STAGE);
+        if (kt > wave_kt_last) continue;                    // every key of this tile is above the diagonal
+        const uint32_t st = lds0 + (kt & 1) * att::STAGE;
+
+        // ---- S^T = K Q^T over d (8 k-steps), K fragments one step ahead
+        f32x16 sacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
+        u32x4 kf[2][2];
+        kf[0][0] = att_read_b128(st + koff[0][0]);
+        kf[0][1] = att_read_b128(st + koff[1][0]);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int cb = ks & 1;
+            if (ks < 7) {
+                kf[cb ^ 1][0] = att_read_b128(st + koff[0][ks + 1]);
+                kf[cb ^ 1][1] = att_read_b128(st + koff[1][ks + 1]);
+                asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(kf[cb][0]), "+v"(kf[cb][1]));
+            } else {
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[cb][0]), "+v"(kf[cb][1]));
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[cb][t]),
+                                                                  __builtin_bit_cast(bf16x8, qf[ks]), sacc[t],
+                                                                  0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- online softmax: lane holds query `query`, keys kt*64 + 32 t + 8 (r/4) + 4 hl + r%4
+        const bool diag = kt * att::BKV + att::BKV - 1 > wq0;
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = sacc[t][r] * scale_log2;
+                if (diag) {
+                    const int key = kt * att::BKV + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (key > query) x = -INFINITY;
+                }
+                sacc[t][r] = x;
+                mloc = fmaxf(mloc, x);
+            }
+        const float m_new = fmaxf(m_run, att_half_max(mloc));   // finite: key 0 of tile 0 is seen by all
+        const float alpha = att_exp2(m_run - m_new);
+        // P^T fragments (B operand): k-step (t, h) holds rows r = 8h .. 8h+7.
+        // The row sum adds the bf16-rounded probabilities that multiply V, so
+        // the weights applied to V sum to one.
+        u32x4 pf[2][2];
+        float lloc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = att_pack_bf16(att_exp2(sacc[t][8 * h + 2 * q] - m_new),
+                                                     att_exp2(sacc[t][8 * h + 2 * q + 1] - m_new));
+                    pf[t][h][q] = w;
+                    lloc += bf16_lo(w) + bf16_hi(w);
+                }
+        l_run = l_run * alpha + att_half_sum(lloc);
+        m_run = m_new;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T += V^T P^T over the tile's keys (4 k-steps x 4 d-tiles)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int t = kk >> 1, h = kk & 1;
+            const uint32_t kb = st + (32 * t + 16 * h) * att::ROWB;
+            u32x2 vr[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2)
+                    vr[mt][e2] = att_read_tr16(kb + (voff_base[e2] ^ (uint32_t)(mt * 64)));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(vr[0][0]), "+v"(vr[0][1]), "+v"(vr[1][0]), "+v"(vr[1][1]),
+                           "+v"(vr[2][0]), "+v"(vr[2][1]), "+v"(vr[3][0]), "+v"(vr[3][1]));
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const u32x4 a = {vr[mt][0].x, vr[mt][0].y, vr[mt][1].x, vr[mt][1].y};
+                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                   __builtin_bit_cast(bf16x8, pf[t][h]), oacc[mt],
+                                                                   0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- O = O^T / l, lane: query `query`, d = 32 mt + 8 gq + 4 hl + (0..3)
+    if (query < S) {
+        const float inv = 1.0f / l_run;
+        uint16_t *orow = O + (bh * (int64_t)S + query) * att::D;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                u32x2 w;
+                w.x = att_pack_bf16(oacc[mt][4 * gq + 0] * inv, oacc[mt][4 * gq + 1] * inv);
+                w.y = att_pack_bf16(oacc[mt][4 * gq + 2] * inv, oacc[mt][4 * gq + 3] * inv);
+                *reinterpret_cast<u32x2 *>(orow + 32 * mt + 8 * gq + 4 * hl) = w;
+            }
+    }
+}
+
+}  // namespace fc
+
+using namespace fc;
+
+extern "C" uint64_t fc_attention_flops(int64_t BH, int S, int D)
+{
+    if (BH < 1 || S < 1 || D < 1) return 0;
+    return 2ull * (uint64_t)D * (uint64_t)S * (uint64_t)(S + 1) * (uint64_t)BH;
+}
+
+extern "C" uint64_t fc_attention_bytes(int64_t BH, int S, int D)
+{
+    if (BH < 1 || S < 1 || D < 1) return 0;
+    return 8ull * (uint64_t)BH * (uint64_t)S * (uint64_t)D;
+}
+
+extern "C" int fc_causal_attention(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O,
+                                   int64_t BH, int S, int D, float scale, fc_stream stream)
+{
+    if (BH < 1 || S < 1 || D < 1) return FC_ERR_SHAPE;
+    if (D != att::D) return FC_ERR_UNSUPPORTED;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return FC_ERR_SHAPE;
+    if (!Q || !K || !V || !O) return FC_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return FC_ERR_ALIGN;
+    const size_t bytes = (size_t)BH * (size_t)S * (size_t)D * 2;
+    if (overlaps(O, bytes, Q, bytes) || overlaps(O, bytes, K, bytes) || overlaps(O, bytes, V, bytes))
+        return FC_ERR_ALIAS;
+    const int64_t nqt = (S + att::BQ - 1) / att::BQ;
+    if (BH * nqt > 0x7fffffff || (int64_t)S * att::D > ((int64_t)1 << 40)) return FC_ERR_UNSUPPORTED;
+    attention_fwd_kernel<<<(unsigned)(BH * nqt), att::NT, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        Q, K, V, O, BH, S, scale * att::LOG2E);
+    return launch_status();
+}

@@ -181,6 +181,40 @@ int fc_causal_mask_materialise(uint16_t *mask, int64_t BH, int S, fc_stream stre
 /* UNFUSED: round_up(2*BH*S*S, 256) + 8*BH*S bytes; FUSED: 0. */
 size_t fc_softmax_workspace_bytes(int64_t BH, int S, int mode);
 
+/* ------------------------------------------------------------ causal attention */
+
+/*
+ * fc_causal_attention -- O = softmax(scale * Q K^T under the causal mask) V in
+ * one kernel that never writes the scores: key/value tiles stream through the
+ * chip while an online softmax keeps each query row's running max and sum
+ * ("AIGC 基本功｜算子融合与 CUDA Graph-Fusion", section 3.5: query i sees keys
+ * j <= i, and key tiles wholly above the diagonal are skipped; its further-
+ * reading list names this online-softmax kernel as the way to remove the
+ * S x S score tensor).
+ *
+ *  Q, K, V  device bf16 [BH, S, D] row-major (head-major rows), 16-byte aligned.
+ *  O        device bf16 [BH, S, D], must not overlap Q, K or V.
+ *  D        128 (FC_ERR_UNSUPPORTED otherwise); S >= 1 (any length: the last
+ *           tiles are ragged); BH >= 1; scale finite (the pages' 1/sqrt(128)).
+ *  Arithmetic: fp32 accumulation of the products; the softmax in fp32 (base-2
+ *  exponent of the pre-scaled scores); the probabilities are rounded to bf16
+ *  before their product with V and the row sum adds those rounded values, so
+ *  the weights applied to V sum to one; O is rounded to bf16 (round to
+ *  nearest even).
+ *
+ *  Returns FC_OK, or FC_ERR_SHAPE / FC_ERR_UNSUPPORTED / FC_ERR_NULL /
+ *  FC_ERR_ALIGN / FC_ERR_ALIAS before anything is launched, or FC_ERR_HIP if
+ *  the launch fails.  No workspace; asynchronous on `stream`.
+ */
+int fc_causal_attention(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O,
+                        int64_t BH, int S, int D, float scale, fc_stream stream);
+
+/* Algorithmic work of fc_causal_attention: flops of the two products over the
+ * kept (j <= i) pairs, 2*D*S*(S+1)*BH; DRAM bytes with Q, K, V read once and O
+ * written once, 8*BH*S*D.  0 for invalid arguments. */
+uint64_t fc_attention_flops(int64_t BH, int S, int D);
+uint64_t fc_attention_bytes(int64_t BH, int S, int D);
+
 /* ------------------------------------------------------------ accounting */
 
 /*

@@ -251,3 +251,19 @@ def test_envelope_validation_before_launch():
     assert L.fce_read(MIS, C, FAKE, None) == fc.FC_ERR_ALIGN
     assert L.fce_mfma(None, 1, None) == fc.FC_ERR_NULL
     assert L.fce_mfma(FAKE, 0, None) == fc.FC_ERR_SHAPE
+
+
+def test_attention_accounting_and_validation():
+    assert fc.fc_attention_flops(1, 1, 128) == 2 * 128 * 1 * 2
+    assert fc.fc_attention_flops(128, 2048, 128) == 2 * 128 * 2048 * 2049 * 128
+    assert fc.fc_attention_bytes(128, 2048, 128) == 8 * 128 * 2048 * 128
+    assert fc.fc_attention_flops(0, 5, 128) == 0 and fc.fc_attention_bytes(1, 0, 128) == 0
+    L = fc.lib()
+    big = 1 << 24
+    assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 64, 0.1, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 0, 128, 0.1, None) == fc.FC_ERR_SHAPE
+    assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 0, 8, 128, 0.1, None) == fc.FC_ERR_SHAPE
+    assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, float("nan"), None) == fc.FC_ERR_SHAPE
+    assert L.fc_causal_attention(None, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, 0.1, None) == fc.FC_ERR_NULL
+    assert L.fc_causal_attention(MIS, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, 0.1, None) == fc.FC_ERR_ALIGN
+    assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 1024, 1, 8, 128, 0.1, None) == fc.FC_ERR_ALIAS

@@ -1,0 +1,104 @@
+"""GPU parity of the one-kernel causal attention (online softmax, scores never
+written) against the fp64 oracle.
+
+Bar, per element: |O - ref| <= 2^-8 (|ref| + max_{j<=i} |V[j, d]|).  The
+kernel rounds each probability to bf16 before its product with V, which moves
+an output by at most 2^-9 times the largest |V| of its column over the causal
+prefix (the weights sum to one), and rounds O to bf16 (2^-9 |O|); the bound is
+twice that.  Everything else (fp32 accumulation of 128-term products and of
+the row sums, the base-2 exponent) is orders of magnitude smaller.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_epilogues_amd as fc  # noqa: E402
+from gpu_util import announce  # noqa: E402
+
+SCALE = 128 ** -0.5
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def run(Q, K, V, scale=SCALE):
+    q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+    o = torch.empty_like(q)
+    fc.fc_causal_attention(q, k, v, o, scale)
+    torch.cuda.synchronize()
+    return o.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def vals(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def colmax_prefix(V):
+    """max_{j<=i} |V[j, d]| for every (head, i, d)."""
+    return np.maximum.accumulate(np.abs(vals(V)), axis=1)
+
+
+def check(out_bits, ref, bound_v):
+    err = np.abs(vals(out_bits) - ref)
+    tol = 2.0 ** -8 * (np.abs(ref) + bound_v)
+    ok = bool(np.all(err <= tol))
+    return ok, float(np.max(err / tol))
+
+
+@pytest.mark.parametrize("BH,S", [(1, 1), (2, 17), (1, 64), (1, 65), (3, 130), (2, 300), (1, 513)])
+def test_small_shapes_all_rows(BH, S):
+    announce(f"attention BH={BH} S={S} all rows")
+    Q, K, V = synth.attention_inputs(BH, S, 128, salt=S)
+    out = run(Q, K, V)
+    ref = oracle.causal_attention_f64(Q, K, V, SCALE)
+    ok, worst = check(out, ref, colmax_prefix(V))
+    assert ok, worst
+
+
+def test_full_config_sampled_rows():
+    """[8*16, 2048, 128] (the softmax workload's heads and length, head dim 128):
+    rows at tile edges and random rows of three heads against the oracle."""
+    BH, S = 128, 2048
+    announce(f"attention full config BH={BH} S={S} sampled rows")
+    Q, K, V = synth.attention_inputs(BH, S, 128)
+    out = run(Q, K, V).reshape(BH * S, 128)
+    rng = np.random.default_rng(1)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 129, 1023, 1024, 2046, 2047]
+    rows = []
+    for h in (0, 77, 127):
+        rows += [h * S + i for i in edges] + list(h * S + rng.integers(0, S, 40))
+    rows = np.array(rows)
+    ref = oracle.causal_attention_rows(Q, K, V, SCALE, rows)
+    cm = colmax_prefix(V).reshape(BH * S, 128)[rows]
+    ok, worst = check(out[rows], ref, cm)
+    assert ok, worst
+
+
+def test_closed_forms_on_the_gpu():
+    """scale 0: every row is the running mean of V; constant V: every row is
+    that constant (exact in bf16)."""
+    BH, S = 2, 200
+    announce("attention closed forms")
+    Q, K, V = synth.attention_inputs(BH, S, 128, salt=3)
+    out = vals(run(Q, K, V, scale=0.0))
+    mean = np.cumsum(vals(V), axis=1) / np.arange(1, S + 1)[None, :, None]
+    assert np.all(np.abs(out - mean) <= 2.0 ** -8 * (np.abs(mean) + colmax_prefix(V)))
+    c = synth.f32_to_bf16_bits(np.linspace(-2, 2, 128).astype(np.float32))
+    Vc = np.broadcast_to(c, V.shape).copy()
+    outc = vals(run(Q, K, Vc))
+    assert np.array_equal(outc, np.broadcast_to(vals(c), outc.shape))
+
+
+def test_deterministic():
+    Q, K, V = synth.attention_inputs(4, 333, 128, salt=9)
+    announce("attention determinism")
+    assert np.array_equal(run(Q, K, V), run(Q, K, V))
