@@ -17,8 +17,9 @@
 //                          the B operand; V^T fragments come from LDS with the
 //                          transposing read ds_read_b64_tr_b16 in the same key
 //                          order as the P registers)
-// The softmax runs in the log2 domain (scores pre-scaled by scale*log2 e,
-// v_exp_f32).  Key tiles entirely above a wave's queries are skipped; tiles
+// The softmax runs in the log2 domain: the running max is taken over the raw
+// scores and the scale (times log2 e) enters once per score, fused into the
+// exponent's argument (v_fma + v_exp_f32); a positive scale is required.  Key tiles entirely above a wave's queries are skipped; tiles
 // that cross its diagonal are masked per element.  Query tiles with the most
 // keys are dispatched first.
 //
@@ -35,6 +36,7 @@
 namespace fc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -154,12 +156,39 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
+    // per-lane element offsets of this wave's load rows inside a full tile, and
+    // the wave-uniform LDS block offsets (used for every tile wholly below S)
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t ioff_k[4], ioff_v[4], lds_blk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int blk = wave_s * 4 + q, r = blk * 4 + (lane >> 4), pu = lane & 15;
+        ioff_k[q] = r * att::D + (pu ^ (r & 15)) * 8;
+        ioff_v[q] = r * att::D + (pu ^ (4 * (r & 3))) * 8;
+        lds_blk[q] = blk * 1024;
+    }
     att_issue(Kh, Vh, S, 0, lds);
     for (int kt = 0; kt <= kt_last; ++kt) {
         __builtin_amdgcn_s_waitcnt(0xF70);                  // vmcnt(0): this wave's share of tile kt landed
         __builtin_amdgcn_s_barrier();                       // every wave's share landed; stage kt-1 is free
         __builtin_amdgcn_sched_barrier(0);
-        if (kt < kt_last) att_issue(Kh, Vh, S, kt + 1, lds + ((kt + 1) & 1) * att::STAGE);
+        if (kt < kt_last) {
+            const int kn = kt + 1;
+            FC_LDS char *stn = lds + (kn & 1) * att::STAGE;
+            if ((kn + 1) * att::BKV <= S) {
+                const uint16_t *kb = Kh + (int64_t)kn * att::BKV * att::D;
+                const uint16_t *vb = Vh + (int64_t)kn * att::BKV * att::D;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    __builtin_amdgcn_global_load_lds((const FC_GLB void *)(kb + ioff_k[q]),
+                                                     (FC_LDS void *)(stn + lds_blk[q]), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds((const FC_GLB void *)(vb + ioff_v[q]),
+                                                     (FC_LDS void *)(stn + att::TILE + lds_blk[q]), 16, 0, 0);
+                }
+            } else {
+                att_issue(Kh, Vh, S, kn, stn);                  // ragged last tile: rows clamped to S-1
+            }
+        }
         if (kt > wave_kt_last) continue;                    // every key of this tile is above the diagonal
         const uint32_t st = lds0 + (kt & 1) * att::STAGE;
 
@@ -190,26 +219,31 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- online softmax: lane holds query `query`, keys kt*64 + 32 t + 8 (r/4) + 4 hl + r%4
-        const bool diag = kt * att::BKV + att::BKV - 1 > wq0;
+        // ---- online softmax: lane holds query `query`, keys kt*64 + 32 t + 8 (r/4) + 4 hl + r%4.
+        // Raw scores are masked and maximised (a positive scale keeps the
+        // order); the scale enters once, fused into each exponent's argument.
+        if (kt * att::BKV + att::BKV - 1 > wq0) {          // tile crosses this wave's diagonal
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * att::BKV + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (key > query) sacc[t][r] = -INFINITY;
+                }
+        }
         float mloc = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sacc[t][r] * scale_log2;
-                if (diag) {
-                    const int key = kt * att::BKV + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (key > query) x = -INFINITY;
-                }
-                sacc[t][r] = x;
-                mloc = fmaxf(mloc, x);
-            }
+            for (int r = 0; r < 16; r += 2)                 // plain v_max3 (no operand canonicalisation)
+                asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mloc) : "v"(mloc), "v"(sacc[t][r]), "v"(sacc[t][r + 1]));
         const float m_new = fmaxf(m_run, att_half_max(mloc));   // finite: key 0 of tile 0 is seen by all
-        const float alpha = att_exp2(m_run - m_new);
+        const float mc = m_new * scale_log2;
+        const float alpha = att_exp2((m_run - m_new) * scale_log2);
         // P^T fragments (B operand): k-step (t, h) holds rows r = 8h .. 8h+7.
-        // The row sum adds the bf16-rounded probabilities that multiply V, so
-        // the weights applied to V sum to one.
+        // The row sum adds the bf16-rounded probabilities that multiply V
+        // (v_dot2 against (1, 1)), so the weights applied to V sum to one.
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
         u32x4 pf[2][2];
         float lloc = 0.0f;
 #pragma unroll
@@ -218,15 +252,18 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t w = att_pack_bf16(att_exp2(sacc[t][8 * h + 2 * q] - m_new),
-                                                     att_exp2(sacc[t][8 * h + 2 * q + 1] - m_new));
+                    const uint32_t w =
+                        att_pack_bf16(att_exp2(__builtin_fmaf(sacc[t][8 * h + 2 * q], scale_log2, -mc)),
+                                      att_exp2(__builtin_fmaf(sacc[t][8 * h + 2 * q + 1], scale_log2, -mc)));
                     pf[t][h][q] = w;
-                    lloc += bf16_lo(w) + bf16_hi(w);
+                    lloc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, lloc, false);
                 }
         l_run = l_run * alpha + att_half_sum(lloc);
         m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {  // no lane's max moved: nothing to rescale
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
+            for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- O^T += V^T P^T over the tile's keys (4 k-steps x 4 d-tiles)
@@ -291,7 +328,7 @@ extern "C" int fc_causal_attention(const uint16_t *Q, const uint16_t *K, const u
 {
     if (BH < 1 || S < 1 || D < 1) return FC_ERR_SHAPE;
     if (D != att::D) return FC_ERR_UNSUPPORTED;
-    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return FC_ERR_SHAPE;
+    if (!(scale > 0.0f) || scale > 3.0e38f) return FC_ERR_SHAPE;   // also rejects NaN
     if (!Q || !K || !V || !O) return FC_ERR_NULL;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return FC_ERR_ALIGN;
     const size_t bytes = (size_t)BH * (size_t)S * (size_t)D * 2;

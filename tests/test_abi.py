@@ -263,7 +263,8 @@ def test_attention_accounting_and_validation():
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 64, 0.1, None) == fc.FC_ERR_UNSUPPORTED
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 0, 128, 0.1, None) == fc.FC_ERR_SHAPE
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 0, 8, 128, 0.1, None) == fc.FC_ERR_SHAPE
-    assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, float("nan"), None) == fc.FC_ERR_SHAPE
+    for bad in (float("nan"), 0.0, -0.1, float("inf")):
+        assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, bad, None) == fc.FC_ERR_SHAPE
     assert L.fc_causal_attention(None, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, 0.1, None) == fc.FC_ERR_NULL
     assert L.fc_causal_attention(MIS, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, 0.1, None) == fc.FC_ERR_ALIGN
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 1024, 1, 8, 128, 0.1, None) == fc.FC_ERR_ALIAS

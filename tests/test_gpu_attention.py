@@ -84,12 +84,12 @@ def test_full_config_sampled_rows():
 
 
 def test_closed_forms_on_the_gpu():
-    """scale 0: every row is the running mean of V; constant V: every row is
-    that constant (exact in bf16)."""
+    """Q = 0: every score is 0, so every row is the running mean of V;
+    constant V: every row is that constant (exact in bf16)."""
     BH, S = 2, 200
     announce("attention closed forms")
     Q, K, V = synth.attention_inputs(BH, S, 128, salt=3)
-    out = vals(run(Q, K, V, scale=0.0))
+    out = vals(run(np.zeros_like(Q), K, V))
     mean = np.cumsum(vals(V), axis=1) / np.arange(1, S + 1)[None, :, None]
     assert np.all(np.abs(out - mean) <= 2.0 ** -8 * (np.abs(mean) + colmax_prefix(V)))
     c = synth.f32_to_bf16_bits(np.linspace(-2, 2, 128).astype(np.float32))
