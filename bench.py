@@ -51,6 +51,7 @@ PLANS = [[1, 1, 1, 1], [1, 3], [2, 2], [4]]
 SM_B, SM_H, SM_S = 8, 16, 2048
 SM_TILES = [64, 128, 256, 2048]
 SCALE = 1.0 / (128.0 ** 0.5)
+ATT_BH, ATT_S, ATT_D = SM_B * SM_H, SM_S, 128   # attention over the softmax workload's heads and length
 
 
 def log(msg):
@@ -170,6 +171,14 @@ def cpu_baseline(budget_s=12.0):
     oracle.gemm_epilogue_at(A, B, bias, R, rr.integers(0, M, cnt), rr.integers(0, N, cnt))
     t_g = time.perf_counter() - t0
     tflops = 2.0 * K * cnt / t_g / 1e12
+    # attention: every query row of 8 [2048, 128] heads (the oracle's cost of
+    # a row grows with its causal prefix)
+    att_heads = 8
+    Qa, Ka, Va = synth.attention_inputs(att_heads, ATT_S, ATT_D, salt=11)
+    t0 = time.perf_counter()
+    oracle.causal_attention_rows(Qa, Ka, Va, SCALE, np.arange(att_heads * ATT_S))
+    t_a = time.perf_counter() - t0
+    att_tflops = 2.0 * ATT_D * ATT_S * (ATT_S + 1) * att_heads / t_a / 1e12
     return {
         "value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": (f"fp64 C oracle on {threads} threads: {chain_passes} pass(es) of the fused chain K in "
@@ -178,6 +187,8 @@ def cpu_baseline(budget_s=12.0):
                    f"kernels' algorithmic bytes for the same work"),
         "gemm_epilogue": {"value": round(tflops, 6), "unit": "TFLOP/s",
                           "sample": f"{cnt} sampled outputs of the 4096^3 chain (2*K flops each) in {t_g:.1f}s"},
+        "attention": {"value": round(att_tflops, 6), "unit": "TFLOP/s",
+                      "sample": f"all query rows of {att_heads} [2048, 128] heads (causal flops) in {t_a:.1f}s"},
     }
 
 
@@ -279,6 +290,16 @@ def measure_torch_rows(torch, stream, groups, bufs):
         def sm(r):
             return torch.softmax((sd.float() * SCALE).masked_fill(mask, float("-inf")), -1).to(torch.bfloat16)
         out["softmax_us"] = round(_median_ms(torch, stream, sm, 1, iters=3) * 1e3, 2)
+    if "attention" in groups:
+        qa, ka, va, kta = bufs["attention"]
+        S = qa.shape[-2]
+        mask = torch.ones((S, S), dtype=torch.bool, device=qa.device).triu(1)
+
+        def att(r):
+            s = torch.matmul(qa, kta).float() * SCALE
+            p = torch.softmax(s.masked_fill(mask, float("-inf")), -1).to(torch.bfloat16)
+            return torch.matmul(p, va)
+        out["attention_us"] = round(_median_ms(torch, stream, att, 1, iters=3) * 1e3, 2)
     torch.cuda.synchronize()
     return out
 
@@ -292,7 +313,7 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one plain 1 GiB device copy before the timed region (a known-size "
                          "kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
-    ap.add_argument("--rows", default="chain,affine,decode,gemm,softmax",
+    ap.add_argument("--rows", default="chain,affine,decode,gemm,softmax,attention",
                     help="comma list of row groups to run (default: all)")
     ap.add_argument("--no-references", action="store_true",
                     help="skip the stream/MFMA reference probes (libfcenv.so) timed after the steps")
@@ -432,6 +453,27 @@ def main():
                lambda r: fc.fc_causal_softmax(sd, out, SCALE, 64, fc.FC_SOFTMAX_UNFUSED, smws))
         steps.append(sm_rows)
 
+    if "attention" in groups:
+        log("inputs: causal attention [128,2048,128] bf16")
+        Qa, Ka, Va = synth.attention_inputs(ATT_BH, ATT_S, ATT_D)
+        qa, ka, va = (torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) for x in (Qa, Ka, Va))
+        del Qa, Ka, Va
+        oa = torch.empty_like(qa)
+        kta = ka.transpose(-1, -2).contiguous()      # batched bf16 products take contiguous operands
+        sc = torch.empty((ATT_BH, ATT_S, ATT_S), dtype=torch.bfloat16, device=dev)
+        pa = torch.empty_like(sc)
+        bufs["attention"] = (qa, ka, va, kta)
+
+        def att_unfused():
+            torch.matmul(qa, kta, out=sc)
+            fc.fc_causal_softmax(sc, pa, SCALE, 64, fc.FC_SOFTMAX_FUSED)
+            torch.matmul(pa, va, out=oa)
+
+        def att_rows(tm, step_i):
+            tm("attention_fused", lambda r: fc.fc_causal_attention(qa, ka, va, oa, SCALE))
+            tm("attention_scores_materialised", lambda r: att_unfused())
+        steps.append(att_rows)
+
     if args.copy_calib:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -539,6 +581,18 @@ def main():
                           "bytes": fc.fc_plan_bytes(M, N, K, plan), "launches": fc.fc_plan_launches(plan),
                           "min_us": round(tm.minimum(name) * 1e3, 2)}
 
+    if "attention" in groups:
+        fl = fc.fc_attention_flops(ATT_BH, ATT_S, ATT_D)
+        ta, tu = tm.median("attention_fused"), tm.median("attention_scores_materialised")
+        comp["attention_fused"] = {
+            "us": round(ta * 1e3, 2), "TFLOPs": round(fl / (ta * 1e-3) / 1e12, 1),
+            "frac_mfma_bf16": round(fl / (ta * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+            "flops": fl, "bytes": fc.fc_attention_bytes(ATT_BH, ATT_S, ATT_D), "launches": 1,
+            "min_us": round(tm.minimum("attention_fused") * 1e3, 2)}
+        comp["attention_scores_materialised"] = {
+            "us": round(tu * 1e3, 2), "over_fused": round(tu / ta, 2), "launches": 3,
+            "note": "QK^T (torch bf16 matmul) -> [128,2048,2048] bf16 scores -> fc fused softmax T64 -> PV"}
+
     value = fused_bytes / (fused_ms * 1e-3) / 1e9 if fused_ms > 0 else None
 
     # roofline of the dominant kernel of `value`: the fused softmax at tile 64
@@ -606,11 +660,22 @@ def main():
             comp["softmax_fused_T2048"]["GBps"] / refs["mix_softmax_T2048"]["GBps"], 4)
     if torch_rows:
         pairs = {"chain_K8_us": ("chain_K8", "fused_us"), "decode_us": ("decode_plan4", "us"),
-                 "gemm_4096_us": ("gemm_plan4", "us"), "softmax_us": ("softmax_fused_T64", "us")}
+                 "gemm_4096_us": ("gemm_plan4", "us"), "softmax_us": ("softmax_fused_T64", "us"),
+                 "attention_us": ("attention_fused", "us")}
         for k, (row, f) in pairs.items():
             if k in torch_rows and row in comp:
                 torch_rows[k.replace("_us", "_speedup_fused_vs_torch")] = round(torch_rows[k] / comp[row][f], 2)
         comp["torch_eager"] = torch_rows
+
+    if "attention" in groups:
+        fl = fc.fc_attention_flops(ATT_BH, ATT_S, ATT_D)
+        t = tm.median("attention_fused") * 1e-3
+        o = {"bound": "mfma", "kernel": "attention_fwd_kernel [128,2048,128] bf16 causal",
+             "achieved": round(fl / t / 1e12, 1), "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4), "avg_launch_us": round(t * 1e6, 2),
+             "algorithmic_flops": fl, "traffic": None}
+        attach_reference(o, "mfma_f16_random", "TFLOPs")
+        others.append(o)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -634,7 +699,8 @@ def main():
             "workload": ("fused pointwise chain n=16,777,216 fp32 K in {2,3,4,6,8} (naive, fused, fat K=4 T=48) "
                          "+ causal scaled softmax [8,16,2048,2048] bf16 (fused tiles 64/128/256/none, unfused "
                          "5-pass + mask) + GEMM+bias+GELU+residual 4096^3 and 16x4096x4096 fp16 plans "
-                         "[1,1,1,1],[1,3],[2,2],[4] + affine chain n=1,048,576 K=8"),
+                         "[1,1,1,1],[1,3],[2,2],[4] + affine chain n=1,048,576 K=8 + causal attention "
+                         "[128,2048,128] bf16 (one kernel vs scores materialised)"),
             "timing": ("HIP event pair per row around " +
                        ("one replay of the row's captured HIP graph" if args.graph else "host launches")),
             "value_definition": "algorithmic bytes of fused chain (K=2,3,4,6,8) + fused softmax (tile 64) / their summed kernel time",
