@@ -5,8 +5,8 @@ leg may import this package.  The product library (``gemm_epilogues_amd``)
 never imports it and shares no code with it.
 
 ``oracle.c`` holds the plain fp64 definitions (chain, GEMM + bias + GELU +
-residual, causal softmax, causal attention); ``ledger.py`` the byte and launch
-ledgers.  This
+residual, causal softmax, causal attention, RMSNorm); ``ledger.py`` the byte
+and launch ledgers.  This
 module builds ``oracle.c`` with gcc and wraps it with ctypes/numpy.
 
 Every function here is pinned by a CPU test against something other than
@@ -64,6 +64,8 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = None
+        lib.oracle_rmsnorm_f64.argtypes = [P, P, I64, I64, D, P]
+        lib.oracle_rmsnorm_f64.restype = None
         lib.oracle_causal_attention_rows.argtypes = [P, P, P, I64, I64, D, P, I64, P]
         lib.oracle_causal_attention_rows.restype = I
         for name, arg in (("oracle_gelu", D), ("oracle_half_to_double", ctypes.c_uint16),
@@ -204,3 +206,15 @@ def causal_attention_f64(Q, K, V, scale: float) -> np.ndarray:
     """All rows of O, shape [BH, S, D] (small inputs only)."""
     BH, S, D = np.shape(Q)
     return causal_attention_rows(Q, K, V, scale, np.arange(BH * S)).reshape(BH, S, D)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def rmsnorm_f64(x, g, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * g per row, fp64, from fp32 x [rows, d] and g [d]."""
+    x, g = _c(x, np.float32), _c(g, np.float32)
+    rows, d = x.shape
+    assert g.shape == (d,)
+    y = np.empty((rows, d), dtype=np.float64)
+    _load().oracle_rmsnorm_f64(_p(x), _p(g), rows, d, float(eps), _p(y))
+    return y

@@ -154,3 +154,17 @@ def softmax_bytes(BH: int, S: int, tile: int, fused: bool, elem_bytes: int = 2,
 
 def softmax_launches(fused: bool) -> int:
     return 1 if fused else 5
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+RMSNORM_PASSES = ("square", "mean", "scale by 1/rms", "gain")
+
+
+def rmsnorm_bytes(n: int, fused: bool, elem_bytes: int = 4) -> int:
+    """The appendix ledger's RMSNorm count ("AIGC 基本功", section 3.2): the
+    unfused form is four passes (square, mean, multiply by the reciprocal
+    root, multiply by the gain), each counted as one read and one write of the
+    n-element tensor; fused, one pass reads x and writes y."""
+    passes = 1 if fused else len(RMSNORM_PASSES)
+    return passes * 2 * n * elem_bytes

@@ -272,3 +272,27 @@ int oracle_causal_attention_rows(const uint16_t *Q, const uint16_t *K, const uin
     }
     return failed ? -1 : 0;
 }
+
+/* ------------------------------------------------------------ RMSNorm */
+
+/*
+ * RMSNorm of each row ("AIGC 基本功", section 3.2 byte ledger and the
+ * appendix ledger's RMSNorm entry: square, mean, multiply by the reciprocal
+ * root, multiply by the gain):
+ *   y[i][j] = x[i][j] / sqrt(mean_j x[i][j]^2 + eps) * g[j]
+ * x: fp32 [rows, d]; g: fp32 [d]; y: fp64 [rows, d].
+ */
+void oracle_rmsnorm_f64(const float *x, const float *g, int64_t rows, int64_t d, double eps,
+                        double *y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const float *xr = x + i * d;
+        double ss = 0.0;
+        for (int64_t j = 0; j < d; ++j)
+            ss += (double)xr[j] * (double)xr[j];
+        const double r = sqrt(ss / (double)d + eps);
+        for (int64_t j = 0; j < d; ++j)
+            y[i * d + j] = (double)xr[j] / r * (double)g[j];
+    }
+}
