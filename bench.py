@@ -52,6 +52,8 @@ SM_B, SM_H, SM_S = 8, 16, 2048
 SM_TILES = [64, 128, 256, 2048]
 SCALE = 1.0 / (128.0 ** 0.5)
 ATT_BH, ATT_S, ATT_D = SM_B * SM_H, SM_S, 128   # attention over the softmax workload's heads and length
+RMS_ROWS, RMS_D, RMS_EPS = 1024, 4096, 1e-5     # n = 4,194,304 fp32 (the ledger's ~4M), rows of d_model 4096
+RMS_SETS = 17                                    # 17 x 32 MiB: ceil(512 MiB / footprint) + 1
 
 
 def log(msg):
@@ -241,6 +243,12 @@ def measure_references(torch, stream, groups, bufs, fc):
             ms = _median_ms(torch, stream, lambda r: env.fce_read(dsets[r][1], nb, sink), DECODE_SETS)
             out["read_32MiB_cold"] = {"GBps": round(nb / ms / 1e6, 1), "bytes": nb,
                                       "probe": f"fce_read of B, {DECODE_SETS} rotating copies"}
+        if "rmsnorm" in groups:
+            rsets, _ = bufs["rmsnorm"]
+            nb = rsets[0][0].numel() * 4
+            ms = _median_ms(torch, stream, lambda r: env.fce_mix(rsets[r][0], nb, rsets[r][1], nb), RMS_SETS)
+            out["copy_16MiB_cold"] = {"GBps": round(2 * nb / ms / 1e6, 1), "bytes": 2 * nb,
+                                      "probe": f"fce_mix read 16 MiB + write 16 MiB, {RMS_SETS} rotating sets"}
         if "gemm" in groups:
             msink = torch.empty(env.fce_mfma_sink_floats(), dtype=torch.float32, device=dev)
             iters = 2000
@@ -290,6 +298,12 @@ def measure_torch_rows(torch, stream, groups, bufs):
         def sm(r):
             return torch.softmax((sd.float() * SCALE).masked_fill(mask, float("-inf")), -1).to(torch.bfloat16)
         out["softmax_us"] = round(_median_ms(torch, stream, sm, 1, iters=3) * 1e3, 2)
+    if "rmsnorm" in groups:
+        rsets, grms = bufs["rmsnorm"]
+        out["rmsnorm_us"] = round(_median_ms(
+            torch, stream,
+            lambda r: rsets[r][0] * torch.rsqrt(rsets[r][0].pow(2).mean(-1, keepdim=True) + RMS_EPS) * grms,
+            RMS_SETS) * 1e3, 2)
     if "attention" in groups:
         qa, ka, va, kta = bufs["attention"]
         S = qa.shape[-2]
@@ -313,7 +327,7 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one plain 1 GiB device copy before the timed region (a known-size "
                          "kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
-    ap.add_argument("--rows", default="chain,affine,decode,gemm,softmax,attention",
+    ap.add_argument("--rows", default="chain,affine,decode,gemm,softmax,attention,rmsnorm",
                     help="comma list of row groups to run (default: all)")
     ap.add_argument("--no-references", action="store_true",
                     help="skip the stream/MFMA reference probes (libfcenv.so) timed after the steps")
@@ -474,6 +488,25 @@ def main():
             tm("attention_scores_materialised", lambda r: att_unfused())
         steps.append(att_rows)
 
+    if "rmsnorm" in groups:
+        log("inputs: rmsnorm [1024,4096] fp32")
+        rsets = []
+        rg = np.random.default_rng(5)
+        for r in range(RMS_SETS):
+            xr = torch.from_numpy(rg.standard_normal((RMS_ROWS, RMS_D), dtype=np.float32)).to(dev)
+            rsets.append((xr, torch.empty_like(xr)))
+        grms = torch.from_numpy((1.0 + 0.1 * rg.standard_normal(RMS_D)).astype(np.float32)).to(dev)
+        rws = torch.empty(fc.fc_rmsnorm_workspace_bytes(RMS_ROWS, RMS_D, fc.FC_RMSNORM_UNFUSED),
+                          dtype=torch.uint8, device=dev)
+        bufs["rmsnorm"] = (rsets, grms)
+
+        def rms_rows(tm, step_i):
+            tm("rmsnorm_fused", lambda r: fc.fc_rmsnorm(rsets[r][0], grms, rsets[r][1], RMS_EPS,
+                                                        fc.FC_RMSNORM_FUSED), reps=RMS_SETS)
+            tm("rmsnorm_unfused", lambda r: fc.fc_rmsnorm(rsets[r][0], grms, rsets[r][1], RMS_EPS,
+                                                          fc.FC_RMSNORM_UNFUSED, rws), reps=RMS_SETS)
+        steps.append(rms_rows)
+
     if args.copy_calib:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -593,6 +626,17 @@ def main():
             "us": round(tu * 1e3, 2), "over_fused": round(tu / ta, 2), "launches": 3,
             "note": "QK^T (torch bf16 matmul) -> [128,2048,2048] bf16 scores -> fc fused softmax T64 -> PV"}
 
+    if "rmsnorm" in groups:
+        bf = fc.fc_rmsnorm_bytes(RMS_ROWS, RMS_D, fc.FC_RMSNORM_FUSED)
+        bu = fc.fc_rmsnorm_bytes(RMS_ROWS, RMS_D, fc.FC_RMSNORM_UNFUSED)
+        tf_, tu_ = tm.median("rmsnorm_fused"), tm.median("rmsnorm_unfused")
+        comp["rmsnorm_1024x4096"] = {
+            "fused_us": round(tf_ * 1e3, 2), "unfused_us": round(tu_ * 1e3, 2),
+            "unfused_over_fused": round(tu_ / tf_, 2),
+            "fused_GBps": round(bf / (tf_ * 1e-3) / 1e9, 1),
+            "fused_frac_hbm": round(bf / (tf_ * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "ledger_bytes_fused": bf, "ledger_bytes_unfused": bu, "launches_fused": 1, "launches_unfused": 4}
+
     value = fused_bytes / (fused_ms * 1e-3) / 1e9 if fused_ms > 0 else None
 
     # roofline of the dominant kernel of `value`: the fused softmax at tile 64
@@ -661,12 +705,21 @@ def main():
     if torch_rows:
         pairs = {"chain_K8_us": ("chain_K8", "fused_us"), "decode_us": ("decode_plan4", "us"),
                  "gemm_4096_us": ("gemm_plan4", "us"), "softmax_us": ("softmax_fused_T64", "us"),
-                 "attention_us": ("attention_fused", "us")}
+                 "attention_us": ("attention_fused", "us"), "rmsnorm_us": ("rmsnorm_1024x4096", "fused_us")}
         for k, (row, f) in pairs.items():
             if k in torch_rows and row in comp:
                 torch_rows[k.replace("_us", "_speedup_fused_vs_torch")] = round(torch_rows[k] / comp[row][f], 2)
         comp["torch_eager"] = torch_rows
 
+    if "rmsnorm" in groups:
+        b = fc.fc_rmsnorm_bytes(RMS_ROWS, RMS_D, fc.FC_RMSNORM_FUSED)
+        t = tm.median("rmsnorm_fused") * 1e-3
+        o = {"bound": "hbm", "kernel": "rmsnorm_fused_kernel<4> [1024,4096] fp32",
+             "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 2),
+             "algorithmic_bytes": b, "traffic": None}
+        attach_reference(o, "copy_16MiB_cold", "GBps")
+        others.append(o)
     if "attention" in groups:
         fl = fc.fc_attention_flops(ATT_BH, ATT_S, ATT_D)
         t = tm.median("attention_fused") * 1e-3
@@ -700,7 +753,8 @@ def main():
                          "+ causal scaled softmax [8,16,2048,2048] bf16 (fused tiles 64/128/256/none, unfused "
                          "5-pass + mask) + GEMM+bias+GELU+residual 4096^3 and 16x4096x4096 fp16 plans "
                          "[1,1,1,1],[1,3],[2,2],[4] + affine chain n=1,048,576 K=8 + causal attention "
-                         "[128,2048,128] bf16 (one kernel vs scores materialised)"),
+                         "[128,2048,128] bf16 (one kernel vs scores materialised) + RMSNorm [1024,4096] fp32 "
+                         "(fused vs 4 passes)"),
             "timing": ("HIP event pair per row around " +
                        ("one replay of the row's captured HIP graph" if args.graph else "host launches")),
             "value_definition": "algorithmic bytes of fused chain (K=2,3,4,6,8) + fused softmax (tile 64) / their summed kernel time",

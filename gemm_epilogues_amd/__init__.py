@@ -35,6 +35,8 @@ FC_CHAIN_FUSED = 1
 FC_CHAIN_FAT = 2
 FC_SOFTMAX_FUSED = 0
 FC_SOFTMAX_UNFUSED = 1
+FC_RMSNORM_FUSED = 0
+FC_RMSNORM_UNFUSED = 1
 FC_CHAIN_MAX_STAGES = 32
 
 if not os.path.exists(LIB_PATH):
@@ -89,6 +91,9 @@ _SIGS = {
     "fc_causal_attention": (_I, [_P, _P, _P, _P, _I64, _I, _I, _F, _P]),
     "fc_attention_flops": (_U64, [_I64, _I, _I]),
     "fc_attention_bytes": (_U64, [_I64, _I, _I]),
+    "fc_rmsnorm": (_I, [_P, _P, _P, _I64, _I, _F, _I, _P, _SZ, _P]),
+    "fc_rmsnorm_workspace_bytes": (_SZ, [_I64, _I, _I]),
+    "fc_rmsnorm_bytes": (_U64, [_I64, _I, _I]),
     "fc_status_string": (ctypes.c_char_p, [_I]),
     "fc_version": (ctypes.c_char_p, []),
 }
@@ -331,6 +336,36 @@ def fc_attention_flops(BH: int, S: int, D: int) -> int:
 
 def fc_attention_bytes(BH: int, S: int, D: int) -> int:
     return int(_lib.fc_attention_bytes(int(BH), int(S), int(D)))
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def fc_rmsnorm_workspace_bytes(rows: int, d: int, mode: int) -> int:
+    return int(_lib.fc_rmsnorm_workspace_bytes(int(rows), int(d), int(mode)))
+
+
+def fc_rmsnorm_bytes(rows: int, d: int, mode: int) -> int:
+    return int(_lib.fc_rmsnorm_bytes(int(rows), int(d), int(mode)))
+
+
+def fc_rmsnorm(x, g, y, eps: float, mode: int = FC_RMSNORM_FUSED, workspace=None, stream=None) -> None:
+    """y = x / sqrt(mean(x^2, row) + eps) * g; fp32 device tensors x, y [rows, d], g [d]."""
+    torch = _torch()
+    for t, nm in ((x, "x"), (g, "g"), (y, "y")):
+        _dev(t, torch.float32, nm)
+    if x.dim() != 2 or y.shape != x.shape or g.numel() != x.shape[1]:
+        raise ValueError("x, y must be [rows, d] and g [d]")
+    rows, d = x.shape
+    ws_bytes = 0
+    if workspace is None and mode == FC_RMSNORM_UNFUSED:
+        need = fc_rmsnorm_workspace_bytes(rows, d, mode)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.fc_rmsnorm(_ptr(x), _ptr(g), _ptr(y), int(rows), int(d), float(eps), int(mode),
+                         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "fc_rmsnorm")
 
 
 # ---------------------------------------------------------------- accounting (host only)

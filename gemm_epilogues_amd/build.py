@@ -30,7 +30,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # packed fp32 instructions stay off
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]
-SOURCES = ["chain.hip", "chain_fat.hip", "softmax.hip", "gemm.hip", "attention.hip", "api.cpp"]
+SOURCES = ["chain.hip", "chain_fat.hip", "softmax.hip", "gemm.hip", "attention.hip", "rmsnorm.hip", "api.cpp"]
 # measurement probes (stream and MFMA ceilings), a library of their own
 ENV_SOURCES = ["envelope.hip"]
 

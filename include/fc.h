@@ -43,6 +43,7 @@ enum {
 
 enum { FC_CHAIN_NAIVE = 0, FC_CHAIN_FUSED = 1, FC_CHAIN_FAT = 2 };
 enum { FC_SOFTMAX_FUSED = 0, FC_SOFTMAX_UNFUSED = 1 };
+enum { FC_RMSNORM_FUSED = 0, FC_RMSNORM_UNFUSED = 1 };
 
 #define FC_CHAIN_MAX_STAGES 32
 
@@ -216,6 +217,40 @@ int fc_causal_attention(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
  * written once, 8*BH*S*D.  0 for invalid arguments. */
 uint64_t fc_attention_flops(int64_t BH, int S, int D);
 uint64_t fc_attention_bytes(int64_t BH, int S, int D);
+
+/* ------------------------------------------------------------ RMSNorm */
+
+/*
+ * fc_rmsnorm -- y[i][j] = x[i][j] / sqrt(mean_j x[i][j]^2 + eps) * g[j], fp32
+ * ("AIGC 基本功｜算子融合与 CUDA Graph-Fusion", section 3.2 byte ledger and the
+ * appendix ledger's RMSNorm entry: square, mean, multiply by the reciprocal
+ * root, multiply by the gain; four passes unfused, one fused).
+ *
+ *  x, y   device fp32 [rows, d] row-major; g device fp32 [d]; all 16-byte
+ *         aligned; y must not overlap x or g.
+ *  rows >= 1; d a multiple of 4 with 4 <= d <= 16384 (FC_ERR_UNSUPPORTED
+ *  otherwise); eps finite and >= 0.
+ *  mode   FC_RMSNORM_FUSED: one kernel, one workgroup per row, the row held in
+ *         registers; x read once, y written once.  No workspace.
+ *         FC_RMSNORM_UNFUSED: the four passes as four kernels through the
+ *         workspace (squares, then row means, then x times the reciprocal
+ *         root written over the squares, then the gain).
+ *  workspace  device, >= fc_rmsnorm_workspace_bytes() bytes, 16-byte aligned,
+ *         not overlapping x, g or y (NULL allowed for FUSED).
+ *  Every sum, root and product is fp32; the 1/sqrt is correctly rounded.
+ *  Returns FC_OK or an error code before anything is launched (FC_ERR_HIP if
+ *  a launch fails).
+ */
+int fc_rmsnorm(const float *x, const float *g, float *y, int64_t rows, int d, float eps, int mode,
+               void *workspace, size_t ws_bytes, fc_stream stream);
+
+/* UNFUSED: round_up(4*rows*d, 256) + 4*rows bytes; FUSED: 0. */
+size_t fc_rmsnorm_workspace_bytes(int64_t rows, int d, int mode);
+
+/* The appendix ledger's bytes: every pass reads and writes the n = rows*d
+ * fp32 tensor once, so FUSED 8n and UNFUSED 4 * 8n (the gain vector and the
+ * per-row statistics are not counted).  0 for invalid arguments. */
+uint64_t fc_rmsnorm_bytes(int64_t rows, int d, int mode);
 
 /* ------------------------------------------------------------ accounting */
 

@@ -268,3 +268,25 @@ def test_attention_accounting_and_validation():
     assert L.fc_causal_attention(None, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, 0.1, None) == fc.FC_ERR_NULL
     assert L.fc_causal_attention(MIS, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 128, 0.1, None) == fc.FC_ERR_ALIGN
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 1024, 1, 8, 128, 0.1, None) == fc.FC_ERR_ALIAS
+
+
+def test_rmsnorm_accounting_and_validation():
+    n = 1024 * 4096
+    assert fc.fc_rmsnorm_bytes(1024, 4096, fc.FC_RMSNORM_FUSED) == 8 * n
+    assert fc.fc_rmsnorm_bytes(1024, 4096, fc.FC_RMSNORM_UNFUSED) == 32 * n
+    assert fc.fc_rmsnorm_bytes(0, 4096, 0) == 0 and fc.fc_rmsnorm_bytes(4, 4, 7) == 0
+    assert fc.fc_rmsnorm_workspace_bytes(1024, 4096, fc.FC_RMSNORM_FUSED) == 0
+    assert fc.fc_rmsnorm_workspace_bytes(3, 12, fc.FC_RMSNORM_UNFUSED) == 256 + 12
+    L = fc.lib()
+    big = 1 << 24
+    args = (FAKE, FAKE + big, FAKE + 2 * big)
+    assert L.fc_rmsnorm(*args, 4, 6, 1e-5, 0, None, 0, None) == fc.FC_ERR_UNSUPPORTED      # d % 4
+    assert L.fc_rmsnorm(*args, 4, 16388, 1e-5, 0, None, 0, None) == fc.FC_ERR_UNSUPPORTED  # d too long
+    assert L.fc_rmsnorm(*args, 0, 64, 1e-5, 0, None, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fc_rmsnorm(*args, 4, 64, -1.0, 0, None, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fc_rmsnorm(*args, 4, 64, float("nan"), 0, None, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fc_rmsnorm(*args, 4, 64, 1e-5, 2, None, 0, None) == fc.FC_ERR_UNSUPPORTED
+    assert L.fc_rmsnorm(None, FAKE + big, FAKE + 2 * big, 4, 64, 1e-5, 0, None, 0, None) == fc.FC_ERR_NULL
+    assert L.fc_rmsnorm(MIS, FAKE + big, FAKE + 2 * big, 4, 64, 1e-5, 0, None, 0, None) == fc.FC_ERR_ALIGN
+    assert L.fc_rmsnorm(FAKE, FAKE + big, FAKE + 512, 4, 64, 1e-5, 0, None, 0, None) == fc.FC_ERR_ALIAS
+    assert L.fc_rmsnorm(*args, 4, 64, 1e-5, 1, None, 0, None) == fc.FC_ERR_WORKSPACE
