@@ -74,6 +74,22 @@ _SZ = ctypes.c_size_t
 _U64 = ctypes.c_uint64
 _F = ctypes.c_float
 
+class FcStage(ctypes.Structure):
+    _fields_ = [("writes", ctypes.c_double), ("ext_reads", ctypes.c_double), ("flops", ctypes.c_double),
+                ("live_regs", ctypes.c_int)]
+
+
+FC_COST_MAX_LEVELS = 8
+FC_COST_MAX_STAGES = 16
+
+
+class FcCostModel(ctypes.Structure):
+    _fields_ = [("hbm_bytes_per_s", ctypes.c_double), ("flops_per_s", ctypes.c_double),
+                ("launch_s", ctypes.c_double), ("n_levels", ctypes.c_int),
+                ("reg_level", ctypes.c_int * FC_COST_MAX_LEVELS),
+                ("mem_factor", ctypes.c_double * FC_COST_MAX_LEVELS), ("spill_factor", ctypes.c_double)]
+
+
 _SIGS = {
     "fc_chain": (_I, [_P, _P, _I64, _P, _P, _I, _I, _I, _P, _I, _P]),
     "fc_chain_scratch_floats": (_SZ, [_I64, _I, _I, _I]),
@@ -94,6 +110,9 @@ _SIGS = {
     "fc_rmsnorm": (_I, [_P, _P, _P, _I64, _I, _F, _I, _P, _SZ, _P]),
     "fc_rmsnorm_workspace_bytes": (_SZ, [_I64, _I, _I]),
     "fc_rmsnorm_bytes": (_U64, [_I64, _I, _I]),
+    "fc_segments_time": (ctypes.c_double, [_P, _I, _P, _I, _I, _P]),
+    "fc_best_split": (_I, [_P, _I, _I, _P, _P, _P, _P]),
+    "fc_gemm_epilogue_stages": (_I, [_I64, _I64, _I64, _P]),
     "fc_status_string": (ctypes.c_char_p, [_I]),
     "fc_version": (ctypes.c_char_p, []),
 }
@@ -366,6 +385,51 @@ def fc_rmsnorm(x, g, y, eps: float, mode: int = FC_RMSNORM_FUSED, workspace=None
     rc = _lib.fc_rmsnorm(_ptr(x), _ptr(g), _ptr(y), int(rows), int(d), float(eps), int(mode),
                          _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "fc_rmsnorm")
+
+
+# ---------------------------------------------------------------- cost model (host only)
+
+def cost_model(hbm_bytes_per_s: float, flops_per_s: float, launch_s: float,
+               levels=((255, 1.0),), spill_factor: float = 3.0) -> FcCostModel:
+    """Model parameters; `levels` are (register level, memory-time factor) pairs
+    in increasing register order.  Defaults follow the pages' single 255
+    threshold with factor 3 beyond it."""
+    m = FcCostModel()
+    m.hbm_bytes_per_s, m.flops_per_s, m.launch_s = float(hbm_bytes_per_s), float(flops_per_s), float(launch_s)
+    m.n_levels = len(levels)
+    for i, (r, f) in enumerate(levels):
+        m.reg_level[i], m.mem_factor[i] = int(r), float(f)
+    m.spill_factor = float(spill_factor)
+    return m
+
+
+def _stages(stages):
+    arr = (FcStage * len(stages))()
+    for i, st in enumerate(stages):
+        arr[i] = st if isinstance(st, FcStage) else FcStage(*st)
+    return arr, len(stages)
+
+
+def fc_gemm_epilogue_stages(M: int, N: int, K: int):
+    arr = (FcStage * 4)()
+    _check(_lib.fc_gemm_epilogue_stages(int(M), int(N), int(K), arr), "fc_gemm_epilogue_stages")
+    return [arr[i] for i in range(4)]
+
+
+def fc_segments_time(stages, plan: Sequence[int], elem_bytes: int, model: FcCostModel) -> float:
+    arr, n = _stages(stages)
+    parr, pn = _int_array(plan)
+    return float(_lib.fc_segments_time(arr, n, parr, pn, int(elem_bytes), ctypes.byref(model)))
+
+
+def fc_best_split(stages, elem_bytes: int, model: FcCostModel):
+    """(plan, estimated seconds) with the least estimate over all compositions."""
+    arr, n = _stages(stages)
+    out = (ctypes.c_int * FC_COST_MAX_STAGES)()
+    ln, t = ctypes.c_int(0), ctypes.c_double(0.0)
+    _check(_lib.fc_best_split(arr, n, int(elem_bytes), ctypes.byref(model), out, ctypes.byref(ln),
+                              ctypes.byref(t)), "fc_best_split")
+    return [out[i] for i in range(ln.value)], t.value
 
 
 # ---------------------------------------------------------------- accounting (host only)

@@ -275,6 +275,52 @@ int fc_plan_launches(const int *plan, int plan_len);
 uint64_t fc_chain_bytes(int64_t n, int K, int mode);
 uint64_t fc_softmax_bytes(int64_t BH, int S, int tile, int mode);
 
+/* ------------------------------------------------------------ cost model */
+
+/*
+ * The split-plan time model of "K4 讲解：fusion 的三笔账", section 2 (its time
+ * estimate and best-plan search), host only.  A chain is a list of stages; a
+ * plan cuts it into segments, one kernel each.  A segment's time is
+ *   max(bytes / hbm_bytes_per_s * factor(live registers), flops / flops_per_s)
+ *   + launch_s
+ * where bytes = elem_bytes * (its stages' external reads + the intermediate
+ * written by the previous segment + its own one output), and the live
+ * registers are the sum over its stages.  factor(r) = mem_factor[i] for the
+ * first level with r <= reg_level[i], else spill_factor; the pages' model is
+ * one level {255: 1.0} and spill_factor 3.
+ */
+#define FC_COST_MAX_LEVELS 8
+#define FC_COST_MAX_STAGES 16
+typedef struct {
+    double writes;      /* elements the stage writes */
+    double ext_reads;   /* elements it reads from outside the chain (weights, bias, residual) */
+    double flops;
+    int live_regs;      /* registers the stage keeps live when fused */
+} fc_stage;
+typedef struct {
+    double hbm_bytes_per_s;
+    double flops_per_s;
+    double launch_s;                        /* per-kernel cost */
+    int n_levels;                           /* 0 .. FC_COST_MAX_LEVELS, reg_level strictly increasing */
+    int reg_level[FC_COST_MAX_LEVELS];
+    double mem_factor[FC_COST_MAX_LEVELS];
+    double spill_factor;                    /* factor beyond the last level */
+} fc_cost_model;
+
+/* Estimated seconds of a plan (a composition of n_stages, 1 <= n_stages <=
+ * FC_COST_MAX_STAGES); -1 for invalid arguments. */
+double fc_segments_time(const fc_stage *stages, int n_stages, const int *plan, int plan_len,
+                        int elem_bytes, const fc_cost_model *model);
+
+/* The plan with the least estimate over all 2^(n_stages-1) compositions
+ * (the first one in cut-mask order on ties): plan_out (host, >= n_stages
+ * ints), *plan_len_out, and *t_out (may be NULL).  FC_OK or an error code. */
+int fc_best_split(const fc_stage *stages, int n_stages, int elem_bytes, const fc_cost_model *model,
+                  int *plan_out, int *plan_len_out, double *t_out);
+
+/* The four stages of the GEMM epilogue chain for (M, N, K) into out[4]. */
+int fc_gemm_epilogue_stages(int64_t M, int64_t N, int64_t K, fc_stage *out);
+
 /* Static text for a status code. */
 const char *fc_status_string(int status);
 
