@@ -194,6 +194,93 @@ def cpu_baseline(budget_s=12.0):
     }
 
 
+def measure_model_rows(torch, stream, groups, bufs, fc):
+    """Inputs of the split-plan cost model on this device and the rows that
+    validate it: the per-launch cost of a stream (back-to-back empty kernels),
+    a t(n) = a + b n fit of plain copies, the fat probe's register sweep, and
+    every split plan of both GEMM shapes (eager, and for the decode shape also
+    replayed from a captured HIP graph)."""
+    import json as _json
+    from gemm_epilogues_amd import envelope as env
+    dev = torch.device("cuda", 0)
+    out = {}
+    sink = torch.zeros(64, dtype=torch.float32, device=dev)
+    n_l = 200
+    ms = _median_ms(torch, stream, lambda r: env.fce_empty(256, sink), n_l, iters=9)
+    out["launch_us"] = round(ms * 1e3, 3)
+    # t(n) for plain copies of n bytes (read n + write n), least-squares a + b * 2n
+    big = torch.empty(2 * (256 << 20), dtype=torch.uint8, device=dev)
+    src, dst = big[: 256 << 20], big[256 << 20:]
+    pts = []
+    for nb in (32 << 10, 256 << 10, 2 << 20, 16 << 20, 64 << 20, 256 << 20):
+        reps = 50 if nb <= (2 << 20) else 10
+        t = _median_ms(torch, stream, lambda r, nb=nb: env.fce_mix(src, nb, dst, nb), reps, iters=7) * 1e-3
+        pts.append((2 * nb, t))
+    xs = [p[0] for p in pts]
+    ys = [p[1] for p in pts]
+    mx, my = sum(xs) / len(xs), sum(ys) / len(ys)
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    a = my - b * mx
+    out["copy_t_of_n"] = {"points": [{"bytes": x, "us": round(y * 1e6, 2)} for x, y in pts],
+                          "a_us": round(a * 1e6, 2), "GBps_from_b": round(1.0 / b / 1e9, 1)}
+    del big, src, dst
+    if "chain" in groups:
+        sets, coef = bufs["chain"]
+        a4, b4 = synth_chain_coef(4)
+        res_path = os.path.join(ROOT, "gemm_epilogues_amd", "kernel_resources.json")
+        res = _json.load(open(res_path)) if os.path.exists(res_path) else {}
+        sweep = []
+        t_fused = _median_ms(torch, stream, lambda r: fc.fc_chain(sets[r][0], sets[r][1], a4, b4, True,
+                                                                     fc.FC_CHAIN_FUSED), CHAIN_SETS)
+        for T in (0, 16, 48, 96, 128):
+            sk = torch.empty(fc.fc_chain_scratch_floats(CHAIN_N, 4, fc.FC_CHAIN_FAT, T), dtype=torch.float32,
+                             device=dev)
+            t = _median_ms(torch, stream, lambda r, T=T, sk=sk: fc.fc_chain(sets[r][0], sets[r][1], a4, b4, True,
+                                                                             fc.FC_CHAIN_FAT, sk, T), CHAIN_SETS)
+            key = [k for k in res if "chain_fat_kernel" in k and f"ILi4ELb1ELi{T}E" in k]
+            r = res[key[0]] if key else {}
+            sweep.append({"T": T, "us": round(t * 1e3, 2), "over_fused": round(t / t_fused, 2),
+                          "vgprs": r.get("VGPRs"), "agprs": r.get("AGPRs"),
+                          "waves_per_simd": r.get("Occupancy [waves/SIMD]"),
+                          "scratch_bytes_per_lane": r.get("ScratchSize [bytes/lane]")})
+        out["fat_sweep_K4"] = {"fused_us": round(t_fused * 1e3, 2), "rows": sweep}
+    plans_all = [[4], [3, 1], [1, 3], [2, 2], [2, 1, 1], [1, 2, 1], [1, 1, 2], [1, 1, 1, 1]]
+    meas = {}
+    if "decode" in groups:
+        dsets = bufs["decode"]
+        M, N, K = DECODE_MNK
+        rows = {}
+        for plan in plans_all:
+            t = _median_ms(torch, stream, lambda r, plan=plan: fc.fc_gemm_epilogue(*dsets[r][:5], plan, dsets[r][5]),
+                           DECODE_SETS)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(DECODE_SETS):
+                    fc.fc_gemm_epilogue(*dsets[r][:5], plan, dsets[r][5])
+            tg = _median_ms(torch, stream, lambda r, g=g: g.replay(), 1) / DECODE_SETS
+            rows["".join(map(str, plan))] = {"us": round(t * 1e3, 2), "graph_replay_us": round(tg * 1e3, 2)}
+            meas[("decode", tuple(plan))] = t * 1e-3
+        out["decode_all_plans"] = rows
+    if "gemm" in groups and "gemm_out" in bufs:
+        A, B, bias, R = bufs["gemm"]
+        Y, ws = bufs["gemm_out"]
+        rows = {}
+        for plan in plans_all:
+            t = _median_ms(torch, stream, lambda r, plan=plan: fc.fc_gemm_epilogue(A, B, bias, R, Y, plan, ws), 1,
+                           iters=9)
+            rows["".join(map(str, plan))] = {"us": round(t * 1e3, 2)}
+            meas[("gemm", tuple(plan))] = t * 1e-3
+        out["gemm4096_all_plans"] = rows
+    out["_measured"] = meas
+    torch.cuda.synchronize()
+    return out
+
+
+def synth_chain_coef(K):
+    import synth
+    return synth.chain_inputs(1, K)[1:]
+
+
 def _median_ms(torch, stream, fn, reps, iters=7):
     """Median over `iters` event pairs of the time per call of `reps` calls."""
     ts = []
@@ -331,6 +418,9 @@ def main():
                     help="comma list of row groups to run (default: all)")
     ap.add_argument("--no-references", action="store_true",
                     help="skip the stream/MFMA reference probes (libfcenv.so) timed after the steps")
+    ap.add_argument("--no-model", action="store_true",
+                    help="skip the cost-model calibration and validation rows (launch cost, t(n) fit, "
+                         "fat sweep, all split plans, graph replay) timed after the steps")
     ap.add_argument("--no-torch-rows", action="store_true",
                     help="skip the PyTorch eager (unfused library) rows timed after the steps")
     ap.add_argument("--graph", action="store_true",
@@ -437,8 +527,10 @@ def main():
         td = [torch.from_numpy(v.view(np.int16)).to(dev).view(torch.float16) for v in (A, B, bias, R)]
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
         bufs["gemm"] = td
+        bufs["gemm_out"] = (Y,)
         ws = torch.zeros(max(fc.fc_gemm_workspace_bytes(M, N, K, p) for p in PLANS), dtype=torch.uint8,
                          device=dev)
+        bufs["gemm_out"] = (Y, ws)
 
         def gemm_rows(tm, step_i):
             for plan in PLANS:
@@ -538,6 +630,7 @@ def main():
     ms_per_step = wall / max(args.steps, 1) * 1e3
     log(f"timed region {wall:.3f}s, {ms_per_step:.3f} ms/step")
     refs = {} if args.no_references else measure_references(torch, stream, groups, bufs, fc)
+    model_rows = {} if args.no_model else measure_model_rows(torch, stream, groups, bufs, fc)
     torch_rows = {} if args.no_torch_rows else measure_torch_rows(torch, stream, groups, bufs)
 
     # ---------------------------------------------------------------- derived numbers
@@ -729,6 +822,39 @@ def main():
              "algorithmic_flops": fl, "traffic": None}
         attach_reference(o, "mfma_f16_random", "TFLOPs")
         others.append(o)
+
+    if model_rows:
+        meas = model_rows.pop("_measured", {})
+        launch_s = model_rows["launch_us"] * 1e-6
+        hbm = refs.get("copy_64MiB_cold", {}).get("GBps")
+        mm_us = torch_rows.get("gemm_4096_matmul_only_us") if torch_rows else None
+        if mm_us:
+            flops_ps, p_src = 2.0 * 4096 ** 3 / (mm_us * 1e-6), "torch.matmul fp16 4096^3 (vendor GEMM) rate"
+        elif "mfma_f16_random" in refs:
+            flops_ps, p_src = refs["mfma_f16_random"]["TFLOPs"] * 1e12, "random-operand MFMA probe"
+        else:
+            flops_ps, p_src = None, None
+        if hbm and flops_ps and meas:
+            m = fc.cost_model(hbm * 1e9, flops_ps, launch_s, levels=((512, 1.0),), spill_factor=3.0)
+            val = {"calibration": {"hbm_GBps": hbm, "hbm_source": "copy_64MiB_cold reference",
+                                   "TFLOPs": round(flops_ps / 1e12, 1), "flops_source": p_src,
+                                   "launch_us": model_rows["launch_us"],
+                                   "register_rule": "512 live registers per lane (one wave per SIMD), x3 beyond"}}
+            for shape, (M, N, K) in (("decode", DECODE_MNK), ("gemm", GEMM_MNK)):
+                st = fc.fc_gemm_epilogue_stages(M, N, K)
+                rows = {}
+                for (sh, plan), t in meas.items():
+                    if sh != shape:
+                        continue
+                    pred = fc.fc_segments_time(st, list(plan), 2, m)
+                    rows["".join(map(str, plan))] = {"measured_us": round(t * 1e6, 2), "model_us": round(pred * 1e6, 2),
+                                                     "model_over_measured": round(pred / t, 3)}
+                if rows:
+                    best_model, _ = fc.fc_best_split(st, 2, m)
+                    best_meas = min(((t, p) for (sh, p), t in meas.items() if sh == shape))[1]
+                    val[shape] = {"plans": rows, "model_best": best_model, "measured_best": list(best_meas)}
+            model_rows["validation"] = val
+        comp["cost_model"] = model_rows
 
     cpu = None
     if not args.no_cpu_baseline:

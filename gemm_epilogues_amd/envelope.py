@@ -25,8 +25,10 @@ _lib.fce_read.restype, _lib.fce_read.argtypes = _I, [_P, _SZ, _P, _P]
 _lib.fce_mfma.restype, _lib.fce_mfma.argtypes = _I, [_P, _I, _P]
 _lib.fce_mfma_sink_floats.restype, _lib.fce_mfma_sink_floats.argtypes = _SZ, []
 _lib.fce_mfma_flops.restype, _lib.fce_mfma_flops.argtypes = ctypes.c_double, [_I]
+_lib.fce_empty.restype, _lib.fce_empty.argtypes = _I, [_I, _P, _P]
 
-EXPORTED = ("fce_chunk_bytes", "fce_mix", "fce_read", "fce_mfma", "fce_mfma_sink_floats", "fce_mfma_flops")
+EXPORTED = ("fce_chunk_bytes", "fce_mix", "fce_read", "fce_mfma", "fce_mfma_sink_floats", "fce_mfma_flops",
+            "fce_empty")
 
 
 def _addr(t):
@@ -64,3 +66,7 @@ def fce_mfma_flops(iters: int) -> float:
 
 def fce_mfma(sink, iters: int, stream=None) -> None:
     fc._check(_lib.fce_mfma(_addr(sink), int(iters), _stream(stream)), "fce_mfma")
+
+
+def fce_empty(blocks: int, sink, stream=None) -> None:
+    fc._check(_lib.fce_empty(int(blocks), _addr(sink), _stream(stream)), "fce_empty")

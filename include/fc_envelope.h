@@ -50,6 +50,11 @@ int fce_mfma(float *sink, int iters, fc_stream stream);
 size_t fce_mfma_sink_floats(void);
 double fce_mfma_flops(int iters);
 
+/* fce_empty -- an empty kernel of `blocks` 64-lane workgroups (sink: a device
+ * float never written): back-to-back launches of it time the per-kernel
+ * overhead of a stream. */
+int fce_empty(int blocks, float *sink, fc_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

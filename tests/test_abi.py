@@ -251,6 +251,8 @@ def test_envelope_validation_before_launch():
     assert L.fce_read(MIS, C, FAKE, None) == fc.FC_ERR_ALIGN
     assert L.fce_mfma(None, 1, None) == fc.FC_ERR_NULL
     assert L.fce_mfma(FAKE, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fce_empty(0, FAKE, None) == fc.FC_ERR_SHAPE
+    assert L.fce_empty(4, None, None) == fc.FC_ERR_NULL
 
 
 def test_attention_accounting_and_validation():
