@@ -810,7 +810,8 @@ def main():
         o = {"bound": "hbm", "kernel": "rmsnorm_fused_kernel<4> [1024,4096] fp32",
              "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 2),
-             "algorithmic_bytes": b, "traffic": None}
+             "algorithmic_bytes": b,
+             "traffic": load_traffic("rmsnorm_fused", os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "rmsnorm.hip"))}
         attach_reference(o, "copy_16MiB_cold", "GBps")
         others.append(o)
     if "attention" in groups:
@@ -819,7 +820,9 @@ def main():
         o = {"bound": "mfma", "kernel": "attention_fwd_kernel [128,2048,128] bf16 causal",
              "achieved": round(fl / t / 1e12, 1), "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4), "avg_launch_us": round(t * 1e6, 2),
-             "algorithmic_flops": fl, "traffic": None}
+             "algorithmic_flops": fl, "algorithmic_bytes": fc.fc_attention_bytes(ATT_BH, ATT_S, ATT_D),
+             "traffic": load_traffic("attention_fused",
+                                     os.path.join(ROOT, "gemm_epilogues_amd", "csrc", "attention.hip"))}
         attach_reference(o, "mfma_f16_random", "TFLOPs")
         others.append(o)
 
