@@ -102,3 +102,25 @@ def test_deterministic():
     Q, K, V = synth.attention_inputs(4, 333, 128, salt=9)
     announce("attention determinism")
     assert np.array_equal(run(Q, K, V), run(Q, K, V))
+
+
+def test_long_sequence_sampled_rows():
+    """S = 4096 (64 key tiles for the last query tile), one head."""
+    S = 4096
+    announce(f"attention long sequence S={S}")
+    Q, K, V = synth.attention_inputs(1, S, 128, salt=41)
+    out = run(Q, K, V).reshape(S, 128)
+    rows = np.array([0, 1, 127, 128, 2047, 2048, 4094, 4095])
+    ref = oracle.causal_attention_rows(Q, K, V, SCALE, rows)
+    ok, worst = check(out[rows], ref, colmax_prefix(V).reshape(S, 128)[rows])
+    assert ok, worst
+
+
+def test_many_short_heads():
+    """BH = 300 heads of S = 16: one ragged query and key tile per head."""
+    announce("attention 300 heads of 16")
+    Q, K, V = synth.attention_inputs(300, 16, 128, salt=42)
+    out = run(Q, K, V)
+    ref = oracle.causal_attention_f64(Q, K, V, SCALE)
+    ok, worst = check(out, ref, colmax_prefix(V))
+    assert ok, worst

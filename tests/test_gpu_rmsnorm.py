@@ -55,3 +55,13 @@ def test_zero_rows_give_zero():
     g = np.ones(256, np.float32)
     for mode in (0, 1):
         assert not run(x, g, 1e-5, mode).any()
+
+
+def test_many_short_rows():
+    """65536 rows of 64 (one workgroup per row, most lanes idle)."""
+    announce("rmsnorm 65536 x 64")
+    x, g = inputs(65536, 64, 9)
+    for mode in (0, 1):
+        ref = oracle.rmsnorm_f64(x, g, 1e-5)
+        y = run(x, g, 1e-5, mode).astype(np.float64)
+        assert np.all(np.abs(y - ref) <= 4e-6 * np.abs(ref)), mode

@@ -182,3 +182,23 @@ def test_full_config_unfused_sampled(full_scores):
     got = bf16_vals(bits(out.view(BH * S, S)[torch.from_numpy(rows).cuda()]))
     assert np.max(np.abs(got - ref)) <= 1e-2
     del ws
+
+
+@pytest.mark.parametrize("S,tile", [(8192, 64), (8192, 8192), (8200, 256), (12288, 128)])
+def test_long_rows_sampled(S, tile):
+    """The register-resident kernel's longest rows (S = 8192) and the generic
+    kernel past it (S > 8192): sampled rows against the oracle, the zero
+    pattern and the row sums over the whole output."""
+    announce(f"softmax long rows S={S} tile={tile}")
+    s = synth.softmax_inputs(1, S, salt=S + tile)
+    sd = bf16_from_bits(s)
+    out = torch.empty((1, S, S), dtype=torch.bfloat16, device="cuda")
+    fc.fc_causal_softmax(sd, out, SCALE, tile, fc.FC_SOFTMAX_FUSED)
+    torch.cuda.synchronize()
+    rows = np.unique([r for r in (0, 1, tile - 1, tile, 4095, 4096, S // 2, S - 2, S - 1) if r < S])
+    ref = oracle.causal_softmax_rows(s, SCALE, rows)
+    got = bf16_vals(bits(out.view(S, S)[torch.from_numpy(rows).cuda()]))
+    assert np.max(np.abs(got - ref)) <= 1e-2
+    upper = torch.triu(torch.ones(S, S, dtype=torch.bool, device="cuda"), 1)
+    assert int((out.view(S, S)[upper] != 0).sum()) == 0
+    assert float((out.float().sum(dim=2) - 1.0).abs().max()) <= 2e-2
