@@ -30,6 +30,8 @@
 //                           32-byte column pairs hit 8 different 32-byte slots
 #include "fc_internal.h"
 
+#include <type_traits>
+
 #define FC_LDS __attribute__((address_space(3)))
 #define FC_GLB __attribute__((address_space(1)))
 
@@ -50,17 +52,42 @@ constexpr int LDS_BYTES = 2 * STAGE;          // two stages
 constexpr float LOG2E = 1.4426950408889634f;
 }
 
+// LDS fragment reads with the constant part of the address (stage, key
+// block) in the instruction's 16-bit offset field, so the loop spends no
+// VALU on addresses: the per-lane part is computed once per kernel.
+template <int OFF>
 __device__ __forceinline__ u32x4 att_read_b128(uint32_t addr)
 {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
     u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
     return v;
 }
+template <int OFF>
 __device__ __forceinline__ u32x2 att_read_tr16(uint32_t addr)
 {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
     u32x2 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
     return v;
+}
+
+// v_max3 without the operand canonicalisation the compiler adds to fmaxf
+__device__ __forceinline__ float att_max3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, so loop indices can be template arguments
+template <int I, int N, class F>
+__device__ __forceinline__ void att_static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        att_static_for<I + 1, N>(f);
+    }
 }
 
 // This wave's quarter of key/value tile kt (rows clamped to S-1; such rows
@@ -130,23 +157,29 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + 16 * ks);
     }
 
-    // per-lane LDS byte offsets (within a stage)
-    uint32_t koff[2][8];                                    // [key m-tile][k-step]
+    // per-lane LDS addresses in stage 0 (stage 1 adds STAGE in the offset field)
+    uint32_t ka[2][8];                                      // K: [key m-tile][k-step]
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int r = 32 * t + l32;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) koff[t][ks] = r * att::ROWB + (((2 * ks + hl) ^ (r & 15)) * 16);
+        for (int ks = 0; ks < 8; ++ks) ka[t][ks] = lds0 + r * att::ROWB + (((2 * ks + hl) ^ (r & 15)) * 16);
     }
     // V^T fragments: lane (group g = lane / 16, j = lane % 16) addresses key
-    // k0 + j/4, d = 32 mt + 16 (g & 1) + 4 (j % 4); k0 = 32 t + 16 h + 8 e2 + 4 hl
-    uint32_t voff_base[2];                                  // [e2], for t = h = mt = 0
-    const int g = lane >> 4, j = lane & 15;
+    // k0 + j/4, d = 32 mt + 16 (g & 1) + 4 (j % 4); k0 = 32 t + 16 h + 8 e2 + 4 hl.
+    // The key block (t, h) enters through the offset field; the d-tile mt
+    // meets the swizzle in an XOR, so it gets its own address.
+    uint32_t va[4][2];                                      // [mt][e2], for t = h = 0
+    {
+        const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-        const int key = 8 * e2 + 4 * hl + (j >> 2);        // key & 3 == j >> 2 for every t, h
-        const int unit = (16 * (g & 1) + 4 * (j & 3)) / 8;  // + 4 mt
-        voff_base[e2] = att::TILE + key * att::ROWB + ((unit ^ (4 * (key & 3))) * 16) + (j & 1) * 8;
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const int key = 8 * e2 + 4 * hl + (j >> 2);    // key & 3 == j >> 2 for every t, h
+            const int unit = (16 * (g & 1) + 4 * (j & 3)) / 8;
+            const uint32_t vb = att::TILE + key * att::ROWB + ((unit ^ (4 * (key & 3))) * 16) + (j & 1) * 8;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) va[mt][e2] = lds0 + (vb ^ (uint32_t)(mt * 64));
+        }
     }
 
     f32x16 oacc[4];
@@ -168,13 +201,17 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         lds_blk[q] = blk * 1024;
     }
     att_issue(Kh, Vh, S, 0, lds);
-    for (int kt = 0; kt <= kt_last; ++kt) {
+
+    // One key tile kt, read from stage ST (= kt & 1, a compile-time constant).
+    auto tile = [&](int kt, auto stage) {
+        constexpr int ST = decltype(stage)::value;
+        constexpr int SOFF = ST * att::STAGE;
         __builtin_amdgcn_s_waitcnt(0xF70);                  // vmcnt(0): this wave's share of tile kt landed
         __builtin_amdgcn_s_barrier();                       // every wave's share landed; stage kt-1 is free
         __builtin_amdgcn_sched_barrier(0);
         if (kt < kt_last) {
             const int kn = kt + 1;
-            FC_LDS char *stn = lds + (kn & 1) * att::STAGE;
+            FC_LDS char *stn = lds + (ST ^ 1) * att::STAGE;
             if ((kn + 1) * att::BKV <= S) {
                 const uint16_t *kb = Kh + (int64_t)kn * att::BKV * att::D;
                 const uint16_t *vb = Vh + (int64_t)kn * att::BKV * att::D;
@@ -189,8 +226,7 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
                 att_issue(Kh, Vh, S, kn, stn);                  // ragged last tile: rows clamped to S-1
             }
         }
-        if (kt > wave_kt_last) continue;                    // every key of this tile is above the diagonal
-        const uint32_t st = lds0 + (kt & 1) * att::STAGE;
+        if (kt > wave_kt_last) return;                      // every key of this tile is above the diagonal
 
         // ---- S^T = K Q^T over d (8 k-steps), K fragments one step ahead
         f32x16 sacc[2];
@@ -199,14 +235,13 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
         u32x4 kf[2][2];
-        kf[0][0] = att_read_b128(st + koff[0][0]);
-        kf[0][1] = att_read_b128(st + koff[1][0]);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int cb = ks & 1;
-            if (ks < 7) {
-                kf[cb ^ 1][0] = att_read_b128(st + koff[0][ks + 1]);
-                kf[cb ^ 1][1] = att_read_b128(st + koff[1][ks + 1]);
+        kf[0][0] = att_read_b128<SOFF>(ka[0][0]);
+        kf[0][1] = att_read_b128<SOFF>(ka[1][0]);
+        att_static_for<0, 8>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value, cb = ks & 1;
+            if constexpr (ks < 7) {
+                kf[cb ^ 1][0] = att_read_b128<SOFF>(ka[0][ks + 1]);
+                kf[cb ^ 1][1] = att_read_b128<SOFF>(ka[1][ks + 1]);
                 asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(kf[cb][0]), "+v"(kf[cb][1]));
             } else {
                 asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[cb][0]), "+v"(kf[cb][1]));
@@ -216,7 +251,7 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
                 sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[cb][t]),
                                                                   __builtin_bit_cast(bf16x8, qf[ks]), sacc[t],
                                                                   0, 0, 0);
-        }
+        });
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- online softmax: lane holds query `query`, keys kt*64 + 32 t + 8 (r/4) + 4 hl + r%4.
@@ -231,13 +266,17 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
                     if (key > query) sacc[t][r] = -INFINITY;
                 }
         }
-        float mloc = -INFINITY;
+        // max of the lane's 32 scores and the running max: a v_max3 tree of depth 4
+        float a[11];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2)                 // plain v_max3 (no operand canonicalisation)
-                asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mloc) : "v"(mloc), "v"(sacc[t][r]), "v"(sacc[t][r + 1]));
-        const float m_new = fmaxf(m_run, att_half_max(mloc));   // finite: key 0 of tile 0 is seen by all
+        for (int u = 0; u < 10; ++u) {
+            const int i0 = 3 * u, i1 = i0 + 1, i2 = i0 + 2;
+            a[u] = att_max3(sacc[i0 >> 4][i0 & 15], sacc[i1 >> 4][i1 & 15], sacc[i2 >> 4][i2 & 15]);
+        }
+        a[10] = att_max3(sacc[1][14], sacc[1][15], m_run);
+        const float mloc = att_max3(att_max3(a[0], a[1], a[2]), att_max3(a[3], a[4], a[5]),
+                                    att_max3(a[6], a[7], att_max3(a[8], a[9], a[10])));
+        const float m_new = att_half_max(mloc);             // finite: key 0 of tile 0 is seen by all
         const float mc = m_new * scale_log2;
         const float alpha = att_exp2((m_run - m_new) * scale_log2);
         // P^T fragments (B operand): k-step (t, h) holds rows r = 8h .. 8h+7.
@@ -267,28 +306,31 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- O^T += V^T P^T over the tile's keys (4 k-steps x 4 d-tiles)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int t = kk >> 1, h = kk & 1;
-            const uint32_t kb = st + (32 * t + 16 * h) * att::ROWB;
+        att_static_for<0, 4>([&](auto kkc) {
+            constexpr int kk = decltype(kkc)::value, t = kk >> 1, h = kk & 1;
+            constexpr int VOFF = SOFF + (32 * t + 16 * h) * att::ROWB;
             u32x2 vr[4][2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int e2 = 0; e2 < 2; ++e2)
-                    vr[mt][e2] = att_read_tr16(kb + (voff_base[e2] ^ (uint32_t)(mt * 64)));
+            for (int mt = 0; mt < 4; ++mt) {
+                vr[mt][0] = att_read_tr16<VOFF>(va[mt][0]);
+                vr[mt][1] = att_read_tr16<VOFF>(va[mt][1]);
+            }
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(vr[0][0]), "+v"(vr[0][1]), "+v"(vr[1][0]), "+v"(vr[1][1]),
                            "+v"(vr[2][0]), "+v"(vr[2][1]), "+v"(vr[3][0]), "+v"(vr[3][1]));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const u32x4 a = {vr[mt][0].x, vr[mt][0].y, vr[mt][1].x, vr[mt][1].y};
-                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                const u32x4 av = {vr[mt][0].x, vr[mt][0].y, vr[mt][1].x, vr[mt][1].y};
+                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                    __builtin_bit_cast(bf16x8, pf[t][h]), oacc[mt],
                                                                    0, 0, 0);
             }
-        }
+        });
         __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt <= kt_last; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 <= kt_last) tile(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- O = O^T / l, lane: query `query`, d = 32 mt + 8 gq + 4 hl + (0..3)
