@@ -15,6 +15,8 @@
 // by 16 bytes, which spreads the 16-byte fragment reads across all banks.
 #include "fc_internal.h"
 
+#include <type_traits>
+
 namespace fc {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -476,74 +478,76 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(
 // ------------------------------------------------------------------ ring GEMM (direct-to-LDS, 4 stages)
 
 // 256x256 workgroup tile, 8 waves (two per SIMD) each owning 128x64 (4x2
-// MFMA 32x32x16 tiles), K in 32-deep slabs through a 4-stage LDS ring
-// (4 x 32 KiB).  Slabs are copied global -> LDS by the direct-to-LDS load
+// MFMA 32x32x16 tiles), K in 32-deep slabs through a 4-stage LDS ring.
+// Slabs are copied global -> LDS by buffer loads with the LDS destination
 // (each lane's 16 bytes land at M0 + 16*lane), issued three slabs ahead, so
 // no registers stage the data and HBM latency is covered by three k-steps of
-// MFMAs.  Layouts are XOR-swizzled so every fragment read is bank-conflict
-// free:
-//   A stage: [256 rows][32 k] fp16, 64-byte rows, 16-byte k-unit u stored at
-//            u ^ ((row >> 2) & 3); fragments are ds_read_b128.
-//   B stage: [32 k][256 n] fp16 (B's own row-major layout), 32-byte n-unit v
-//            stored at v ^ (2 * (k & 3)); fragments are k-contiguous by the
-//            transposing read ds_read_b64_tr_b16: within a group of 16 lanes,
-//            lane j addresses B[k0 + j/4][n0 + 4(j%4) .. +3] and lane i gets
-//            B[k0 .. k0+3][n0 + i].
+// MFMAs.  The main loop spends no vector instructions on addresses: the
+// loads take lane-constant byte offsets computed once (the slab enters as a
+// scalar offset for A and as the scalar base of B's buffer descriptor), and
+// the fragment reads take lane-constant LDS addresses with the stage in the
+// instruction's offset field (the loop is unrolled over the four stages).
+// Layouts are XOR-swizzled so every fragment read is bank-conflict free:
+//   A stages (4 x 16 KiB from byte 0): [256 rows][32 k] fp16, 64-byte rows,
+//            16-byte k-unit u stored at u ^ ((row >> 2) & 3); fragments are
+//            ds_read_b128.
+//   B stages (4 x 16 KiB from byte 64 KiB): [32 k][256 n] fp16 (B's own
+//            row-major layout), 32-byte n-unit v stored at v ^ (2 * (k & 3));
+//            fragments are k-contiguous by the transposing read
+//            ds_read_b64_tr_b16: within a group of 16 lanes, lane j addresses
+//            B[k0 + j/4][n0 + 4(j%4) .. +3] and lane i gets B[k0 .. k0+3][n0 + i].
 // A whole k-step of fragments is double-buffered in registers.  Fragment
 // reads are inline asm: the compiler cannot prove they miss the in-flight
 // direct-to-LDS writes and would drain all loads before each read; ordering is
 // instead explicit (vmcnt wait for the slab's own loads, then a barrier), and
 // frag_wait*() ties the fragment registers to an lgkmcnt wait before use.
-// Needs K % 64 == 0 (an even number of slabs); M and N tails read clamped
-// rows/columns whose results are never stored.
+// Needs K % 64 == 0 (an even number of slabs), K <= 2^22 and N <= 2^24 (the
+// lane offsets are 32-bit); M and N tails read clamped rows/columns whose
+// results are never stored.
 namespace ring {
 constexpr int BM = 256, BN = 256, BK = 32, NT = 512, S = 4, WN = 4;
-constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+constexpr int SLAB = BM * BK * 2;            // 16 KiB: one A slab, and one B slab (BN == BM)
+constexpr int BREG = S * SLAB;               // the B stages start at 64 KiB
 constexpr int ROWB = BN * 2;                 // bytes per B k-row in LDS
+constexpr int MAX_K = 1 << 22, MAX_N = 1 << 24;
+// buffer descriptor word 3 for raw 32-bit-format dword loads
+constexpr int RSRC_WORD3 = 0x00020000;
 }  // namespace ring
 
 #define FC_LDS __attribute__((address_space(3)))
 #define FC_GLB __attribute__((address_space(1)))
 
-// This wave's 2 A blocks (16 rows each) and 2 B blocks (2 k-rows each) of one
-// slab, 1 KiB per direct-to-LDS instruction.
-__device__ __forceinline__ void ring_issue(const uint16_t *A, const uint16_t *B, int M, int N, int K,
-                                           int m0, int n0, int slab, FC_LDS char *st)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int k0 = slab * ring::BK;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int blk = wave * 2 + q;
-        const int row = blk * 16 + (lane >> 2);
-        const int u = (lane & 3) ^ ((lane >> 4) & 3);      // logical k-unit of this lane's slot
-        const int gm = min(m0 + row, M - 1);
-        __builtin_amdgcn_global_load_lds((const FC_GLB void *)(A + (int64_t)gm * K + k0 + u * 8),
-                                         (FC_LDS void *)(st + blk * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int blk = wave * 2 + q;
-        const int krow = blk * 2 + (lane >> 5);
-        const int p = (lane & 31) >> 1, half = lane & 1;  // physical 32-byte unit, 16-byte half
-        const int v = p ^ (2 * (krow & 3));
-        const int gn = min(n0 + v * 16 + half * 8, N - 8);
-        __builtin_amdgcn_global_load_lds((const FC_GLB void *)(B + (int64_t)(k0 + krow) * N + gn),
-                                         (FC_LDS void *)(st + ring::A_BYTES + blk * 1024), 16, 0, 0);
-    }
-}
-
-__device__ __forceinline__ f16x8 lds_read_b128(uint32_t addr)
-{
-    f16x8 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
-}
 __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr)
 {
     u32x2 v;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
     return v;
+}
+template <int OFF>
+__device__ __forceinline__ f16x8 ring_read_b128(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+    f16x8 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ring_read_tr16(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, so loop indices can be template arguments
+template <int I, int N, class F>
+__device__ __forceinline__ void ring_static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        ring_static_for<I + 1, N>(f);
+    }
 }
 
 // One k-step's fragments: A [k16][4 tiles], B [k16][2 tiles][2 halves of 4 k].
@@ -571,48 +575,19 @@ __device__ __forceinline__ f16x8 ring_bfrag(const RingFrags &f, int kk, int j)
     return __builtin_bit_cast(f16x8, w);
 }
 
-// Per-lane byte offsets, within a stage, of the 8 A and 8 B fragment reads.
-struct RingAddr {
-    uint32_t a[2][4];
-    uint32_t b[2][2][2];
-};
-__device__ __forceinline__ RingAddr ring_addr(int wm, int wn)
-{
-    RingAddr ad;
-    const int lane = threadIdx.x & 63, r = lane & 31, g = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int u = kk * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + i * 32 + r;
-            ad.a[kk][i] = row * 64 + (u ^ ((row >> 2) & 3)) * 16;
-        }
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            const int v = (wn * 64 + jt * 32 + 16 * (g & 1)) >> 4;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int k = kk * 16 + 8 * (g >> 1) + 4 * hh + (j >> 2);
-                ad.b[kk][jt][hh] = ring::A_BYTES + k * ring::ROWB + (v ^ (2 * (k & 3))) * 32 + (j & 3) * 8;
-            }
-        }
-    }
-    return ad;
-}
-
 template <int LAST>
 __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
     int M, int N, int K, int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) char lds_raw[ring::S * ring::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds_raw[2 * ring::BREG];
     FC_LDS char *lds = (FC_LDS char *)lds_raw;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * ring::BM, n0 = tn * ring::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave / ring::WN, wn = wave % ring::WN;
 
     f32x16 acc[4][2];
@@ -625,55 +600,121 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
 
     const int nk = K / ring::BK;                 // even
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    const RingAddr ad = ring_addr(wm, wn);
-    for (int s = 0; s < ring::S - 1; ++s)
-        ring_issue(A, B, M, N, K, m0, n0, min(s, nk - 1), lds + s * ring::STAGE);
+    // fragment addresses in stage 0 of the A and B regions
+    uint32_t fa[2][4], fb[2][2][2];
+    {
+        const int r = lane & 31, g = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int u = kk * 2 + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * 128 + i * 32 + r;
+                fa[kk][i] = lds0 + row * 64 + (u ^ ((row >> 2) & 3)) * 16;
+            }
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const int v = (wn * 64 + jt * 32 + 16 * (g & 1)) >> 4;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = kk * 16 + 8 * (g >> 1) + 4 * hh + (j >> 2);
+                    fb[kk][jt][hh] = lds0 + ring::BREG + k * ring::ROWB + (v ^ (2 * (k & 3))) * 32 + (j & 3) * 8;
+                }
+            }
+        }
+    }
+    // This wave's 2 A blocks (16 rows each) and 2 B blocks (2 k-rows each) of
+    // every slab, 1 KiB per load instruction: lane byte offsets into the
+    // workgroup's A panel (rows from m0, clamped to M-1; the slab adds 2*k0)
+    // and into one B slab (k-rows from k0, columns from n0 clamped to N-8).
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int blk = wave * 2 + q;
+        const int row = blk * 16 + (lane >> 2);
+        const int u = (lane & 3) ^ ((lane >> 4) & 3);      // logical k-unit of this lane's slot
+        const int gm = min(m0 + row, M - 1);
+        la[q] = (uint32_t)((gm - m0) * K + u * 8) * 2u;
+        const int krow = blk * 2 + (lane >> 5);
+        const int p = (lane & 31) >> 1, half = lane & 1;  // physical 32-byte unit, 16-byte half
+        const int v = p ^ (2 * (krow & 3));
+        const int gn = min(n0 + v * 16 + half * 8, N - 8);
+        lb[q] = (uint32_t)(krow * N + (gn - n0)) * 2u;
+    }
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * K), (short)0, 0x7fffffff, ring::RSRC_WORD3);
+    // slab `slab` into stage ST
+    auto issue = [&](int slab, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        const int k0 = slab * ring::BK;
+        const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(B + (int64_t)k0 * N + n0), (short)0, 0x7fffffff, ring::RSRC_WORD3);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int blk = wave_s * 2 + q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (FC_LDS void *)(lds + ST * ring::SLAB + blk * 1024),
+                                                     16, la[q], k0 * 2, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (FC_LDS void *)(lds + ring::BREG + ST * ring::SLAB + blk * 1024), 16, lb[q], 0, 0, 0);
+        }
+    };
+    issue(0, std::integral_constant<int, 0>{});
+    issue(min(1, nk - 1), std::integral_constant<int, 1>{});
+    issue(min(2, nk - 1), std::integral_constant<int, 2>{});
     __builtin_amdgcn_s_waitcnt(0xF78);           // vmcnt(8): slab 0 of this wave landed
     __builtin_amdgcn_s_barrier();                // ... and of every wave
     RingFrags F[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) F[0].a[kk][i] = lds_read_b128(lds0 + ad.a[kk][i]);
+        for (int i = 0; i < 4; ++i) F[0].a[kk][i] = ring_read_b128<0>(fa[kk][i]);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) F[0].b[kk][jt][hh] = lds_read_tr16(lds0 + ad.b[kk][jt][hh]);
+            for (int hh = 0; hh < 2; ++hh) F[0].b[kk][jt][hh] = ring_read_tr16<0>(fb[kk][jt][hh]);
     }
-    for (int t = 0; t < nk; t += 2) {
+    // k-step tt; H = tt % 4 (the loop base is a multiple of 4), so the stage
+    // read now is H, the one read next H+1 and the one loaded now H+3 (mod 4)
+    auto step = [&](int tt, auto hc) __attribute__((always_inline)) {
+        constexpr int H = decltype(hc)::value, cb = H & 1, nb = cb ^ 1;
+        constexpr int SNEXT = ((H + 1) & 3) * ring::SLAB, SLOAD = (H + 3) & 3;
+        frag_wait0(F[cb]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {            // register buffer index stays static
-            const int tt = t + h, cb = h, nb = h ^ 1;
-            frag_wait0(F[cb]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 0, j), F[cb].a[0][i],
-                                                                       acc[i][j], 0, 0, 0);
-            // slab tt+3 goes to the stage read for step tt-1: every wave read
-            // its fragments for step tt-1 during step tt-2 and waited for all
-            // of them before the barrier of step tt-1; past the end a clamped
-            // re-read lands in a stage that is never read
-            ring_issue(A, B, M, N, K, m0, n0, min(tt + ring::S - 1, nk - 1),
-                       lds + ((tt + ring::S - 1) % ring::S) * ring::STAGE);
-            __builtin_amdgcn_s_waitcnt(0xF78);   // vmcnt(8): slab tt+1 of this wave landed
-            frag_wait1(F[cb]);                   // every fragment read of stage tt done
-            __builtin_amdgcn_s_barrier();        // ... in every wave, and slab tt+1 landed
-            __builtin_amdgcn_sched_barrier(0);
-            const uint32_t st = lds0 + ((tt + 1) % ring::S) * ring::STAGE;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int i = q >> 1, j = q & 1;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 1, j), F[cb].a[1][i],
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 0, j), F[cb].a[0][i],
                                                                    acc[i][j], 0, 0, 0);
-                const int kk = q >> 2, rr = q & 3;   // next step's k16-step-0 frags first
-                F[nb].a[kk][rr] = lds_read_b128(st + ad.a[kk][rr]);
-                F[nb].b[kk][rr >> 1][rr & 1] = lds_read_tr16(st + ad.b[kk][rr >> 1][rr & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        // slab tt+3 goes to the stage read for step tt-1: every wave read its
+        // fragments for step tt-1 during step tt-2 and waited for all of them
+        // before the barrier of step tt-1; past the end a clamped re-read
+        // lands in a stage that is never read
+        issue(min(tt + ring::S - 1, nk - 1), std::integral_constant<int, SLOAD>{});
+        __builtin_amdgcn_s_waitcnt(0xF78);       // vmcnt(8): slab tt+1 of this wave landed
+        frag_wait1(F[cb]);                       // every fragment read of stage tt done
+        __builtin_amdgcn_s_barrier();            // ... in every wave, and slab tt+1 landed
+        __builtin_amdgcn_sched_barrier(0);
+        ring_static_for<0, 8>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value, i = q >> 1, j = q & 1;
+            constexpr int kk = q >> 2, rr = q & 3;   // next step's k16-step-0 frags first
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 1, j), F[cb].a[1][i], acc[i][j],
+                                                               0, 0, 0);
+            F[nb].a[kk][rr] = ring_read_b128<SNEXT>(fa[kk][rr]);
+            F[nb].b[kk][rr >> 1][rr & 1] = ring_read_tr16<SNEXT>(fb[kk][rr >> 1][rr & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    int t = 0;
+    for (; t + 4 <= nk; t += 4) {
+        step(t + 0, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+        step(t + 2, std::integral_constant<int, 2>{});
+        step(t + 3, std::integral_constant<int, 3>{});
+    }
+    if (t < nk) {                                // nk % 4 == 2
+        step(t + 0, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
     }
     __builtin_amdgcn_s_waitcnt(0xF70);           // drain the clamped prefetches
     frag_wait0(F[0]);
@@ -1055,7 +1096,7 @@ static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bia
     const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (big_tiles >= 128) {
         const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
-        if (K % 64 == 0) {
+        if (K % 64 == 0 && K <= ring::MAX_K && N <= ring::MAX_N) {
             gemm_ring_kernel<LAST><<<tiles_m * tiles_n, ring::NT, 0, s>>>(A, B, bias, R, out, M, N, K,
                                                                          tiles_m, tiles_n);
             return launch_status();
