@@ -19,9 +19,12 @@
 //                          order as the P registers)
 // The softmax runs in the log2 domain: the running max is taken over the raw
 // scores and the scale (times log2 e) enters once per score, fused into the
-// exponent's argument (v_fma + v_exp_f32); a positive scale is required.  Key tiles entirely above a wave's queries are skipped; tiles
-// that cross its diagonal are masked per element.  Query tiles with the most
-// keys are dispatched first.
+// exponent's argument (v_fma + v_exp_f32); a positive scale is required.  The
+// reference subtracted in the exponents trails the running max by at most 8
+// (a factor 2^8; it is moved only past that), so the output rescale is rare.
+// Key tiles entirely above a wave's queries are skipped; tiles that cross its
+// diagonal are masked per element.  Query tiles with the most keys are
+// dispatched first.
 //
 // LDS swizzles (16-byte units u of a 256-byte key row r):
 //   K: u ^ (r & 15)      -- the b128 fragment reads of 16 consecutive keys hit
@@ -50,6 +53,10 @@ constexpr int TILE = BKV * ROWB;              // 16 KiB
 constexpr int STAGE = 2 * TILE;               // K tile, then V tile
 constexpr int LDS_BYTES = 2 * STAGE;          // two stages
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LAZY = 8.0f;                  // base-2 exponent slack of the running reference
+constexpr int MAX_S = 1 << 22;                // byte offsets inside one head stay 32-bit
+// buffer descriptor word 3 for raw 32-bit-format dword loads
+constexpr int RSRC_WORD3 = 0x00020000;
 }
 
 // LDS fragment reads with the constant part of the address (stage, key
@@ -189,17 +196,23 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    // per-lane element offsets of this wave's load rows inside a full tile, and
-    // the wave-uniform LDS block offsets (used for every tile wholly below S)
+    // Tiles wholly below S load through buffer descriptors of this head's K and
+    // V: per-lane byte offsets of this wave's rows inside a tile (computed once),
+    // the tile as a scalar offset and the LDS block as a scalar M0, so the load
+    // issue costs no vector instructions.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t ioff_k[4], ioff_v[4], lds_blk[4];
+    uint32_t boff_k[4], boff_v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int blk = wave_s * 4 + q, r = blk * 4 + (lane >> 4), pu = lane & 15;
-        ioff_k[q] = r * att::D + (pu ^ (r & 15)) * 8;
-        ioff_v[q] = r * att::D + (pu ^ (4 * (r & 3))) * 8;
-        lds_blk[q] = blk * 1024;
+        const int blk = wave * 4 + q, r = blk * 4 + (lane >> 4), pu = lane & 15;
+        boff_k[q] = (uint32_t)(r * att::D + (pu ^ (r & 15)) * 8) * 2u;
+        boff_v[q] = (uint32_t)(r * att::D + (pu ^ (4 * (r & 3))) * 8) * 2u;
     }
+    const int head_bytes = S * att::ROWB;
+    const __amdgpu_buffer_rsrc_t rsrc_k =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, head_bytes, att::RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rsrc_v =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, head_bytes, att::RSRC_WORD3);
     att_issue(Kh, Vh, S, 0, lds);
 
     // One key tile kt, read from stage ST (= kt & 1, a compile-time constant).
@@ -213,14 +226,14 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
             const int kn = kt + 1;
             FC_LDS char *stn = lds + (ST ^ 1) * att::STAGE;
             if ((kn + 1) * att::BKV <= S) {
-                const uint16_t *kb = Kh + (int64_t)kn * att::BKV * att::D;
-                const uint16_t *vb = Vh + (int64_t)kn * att::BKV * att::D;
+                const int toff = kn * att::BKV * att::ROWB;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    __builtin_amdgcn_global_load_lds((const FC_GLB void *)(kb + ioff_k[q]),
-                                                     (FC_LDS void *)(stn + lds_blk[q]), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds((const FC_GLB void *)(vb + ioff_v[q]),
-                                                     (FC_LDS void *)(stn + att::TILE + lds_blk[q]), 16, 0, 0);
+                    const int blk = wave_s * 4 + q;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_k, (FC_LDS void *)(stn + blk * 1024), 16,
+                                                             boff_k[q], toff, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (FC_LDS void *)(stn + att::TILE + blk * 1024),
+                                                             16, boff_v[q], toff, 0, 0);
                 }
             } else {
                 att_issue(Kh, Vh, S, kn, stn);                  // ragged last tile: rows clamped to S-1
@@ -276,7 +289,12 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         a[10] = att_max3(sacc[1][14], sacc[1][15], m_run);
         const float mloc = att_max3(att_max3(a[0], a[1], a[2]), att_max3(a[3], a[4], a[5]),
                                     att_max3(a[6], a[7], att_max3(a[8], a[9], a[10])));
-        const float m_new = att_half_max(mloc);             // finite: key 0 of tile 0 is seen by all
+        // The reference m_run trails the row max lazily: it moves only when the
+        // max passes it by more than LAZY in the base-2 exponent, so that
+        // probabilities stay <= 2^LAZY (exact in fp32, no loss in bf16's
+        // relative rounding) and the output rescale below is rarely needed.
+        const float m_max = att_half_max(mloc);             // >= m_run, which entered the max
+        const float m_new = ((m_max - m_run) * scale_log2 > att::LAZY) ? m_max : m_run;  // finite after tile 0
         const float mc = m_new * scale_log2;
         const float alpha = att_exp2((m_run - m_new) * scale_log2);
         // P^T fragments (B operand): k-step (t, h) holds rows r = 8h .. 8h+7.
@@ -299,7 +317,7 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
                 }
         l_run = l_run * alpha + att_half_sum(lloc);
         m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {  // no lane's max moved: nothing to rescale
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {  // no lane's reference moved: nothing to rescale
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
         }
@@ -377,7 +395,7 @@ extern "C" int fc_causal_attention(const uint16_t *Q, const uint16_t *K, const u
     if (overlaps(O, bytes, Q, bytes) || overlaps(O, bytes, K, bytes) || overlaps(O, bytes, V, bytes))
         return FC_ERR_ALIAS;
     const int64_t nqt = (S + att::BQ - 1) / att::BQ;
-    if (BH * nqt > 0x7fffffff || (int64_t)S * att::D > ((int64_t)1 << 40)) return FC_ERR_UNSUPPORTED;
+    if (BH * nqt > 0x7fffffff || S > att::MAX_S) return FC_ERR_UNSUPPORTED;
     attention_fwd_kernel<<<(unsigned)(BH * nqt), att::NT, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         Q, K, V, O, BH, S, scale * att::LOG2E);
     return launch_status();

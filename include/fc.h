@@ -195,12 +195,14 @@ size_t fc_softmax_workspace_bytes(int64_t BH, int S, int mode);
  *
  *  Q, K, V  device bf16 [BH, S, D] row-major (head-major rows), 16-byte aligned.
  *  O        device bf16 [BH, S, D], must not overlap Q, K or V.
- *  D        128 (FC_ERR_UNSUPPORTED otherwise); S >= 1 (any length: the last
- *           tiles are ragged); BH >= 1; scale finite and > 0 (the pages'
- *           1/sqrt(128); FC_ERR_SHAPE otherwise).
+ *  D        128 (FC_ERR_UNSUPPORTED otherwise); 1 <= S <= 2^22 (any length:
+ *           the last tiles are ragged; longer S returns FC_ERR_UNSUPPORTED);
+ *           BH >= 1; scale finite and > 0 (the pages' 1/sqrt(128);
+ *           FC_ERR_SHAPE otherwise).
  *  Arithmetic: fp32 accumulation of the products; the softmax in fp32 (base-2
- *  exponent of scale*log2(e) times the score minus the running max); the
- *  probabilities are rounded to bf16
+ *  exponent of scale*log2(e) times the score minus a running reference that
+ *  trails the row max by at most 8 in the exponent, so probabilities are <= 2^8);
+ *  the probabilities are rounded to bf16
  *  before their product with V and the row sum adds those rounded values, so
  *  the weights applied to V sum to one; O is rounded to bf16 (round to
  *  nearest even).

@@ -263,6 +263,9 @@ def test_attention_accounting_and_validation():
     L = fc.lib()
     big = 1 << 24
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 8, 64, 0.1, None) == fc.FC_ERR_UNSUPPORTED
+    far = 1 << 31                                 # S past 2^22: byte offsets inside a head would pass 2^31
+    assert L.fc_causal_attention(FAKE, FAKE + far, FAKE + 2 * far, FAKE + 3 * far, 1, (1 << 22) + 1, 128, 0.1,
+                                 None) == fc.FC_ERR_UNSUPPORTED
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 1, 0, 128, 0.1, None) == fc.FC_ERR_SHAPE
     assert L.fc_causal_attention(FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, 0, 8, 128, 0.1, None) == fc.FC_ERR_SHAPE
     for bad in (float("nan"), 0.0, -0.1, float("inf")):
