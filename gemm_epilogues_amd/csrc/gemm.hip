@@ -27,34 +27,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Epilogue operators applied after the GEMM, in chain order.
 enum { OP_BIAS = 1, OP_GELU = 2, OP_RES = 3 };
 
-// erfc by the Chebyshev fit of Press et al., Numerical Recipes, section 6.2
-// (erfcc): for z = |x|, t = 1/(1 + z/2),
-//   erfc(z) = t exp(-z^2 - 1.26551223 + t(1.00002368 + t(0.37409196 + ...)))
-// with relative error below 1.2e-7 everywhere, and erfc(-z) = 2 - erfc(z).
-// The relative accuracy carries into GELU's negative tail, where the result
-// is tiny.  About a third of the instructions of the library erff.
-__device__ __forceinline__ float erfc_cheb(float x)
-{
-    const float z = fabsf(x);
-    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
-    float p = 0.17087277f;
-    p = __builtin_fmaf(p, t, -0.82215223f);
-    p = __builtin_fmaf(p, t, 1.48851587f);
-    p = __builtin_fmaf(p, t, -1.13520398f);
-    p = __builtin_fmaf(p, t, 0.27886807f);
-    p = __builtin_fmaf(p, t, -0.18628806f);
-    p = __builtin_fmaf(p, t, 0.09678418f);
-    p = __builtin_fmaf(p, t, 0.37409196f);
-    p = __builtin_fmaf(p, t, 1.00002368f);
-    p = __builtin_fmaf(p, t, -1.26551223f);
-    const float r = t * __builtin_amdgcn_exp2f(__builtin_fmaf(-z, z, p) * 1.4426950408889634f);
-    return x >= 0.0f ? r : 2.0f - r;
-}
-
-// GELU in erf form, z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2)) = 0.5 z erfc(-z / sqrt 2).
+// GELU in erf form, z * Phi(z), Phi the standard normal CDF.  With
+// h = erfc(|z| / sqrt 2) / 2, Phi(z) is 1 - h for z >= 0 and h for z < 0, so
+//   GELU(z) = max(z, 0) - |z| h,
+// one max and one fma after h (relative accuracy of h carries into the
+// negative tail, where the result is tiny).  erfc by the Chebyshev fit of
+// Press et al., Numerical Recipes, section 6.2 (erfcc): for x >= 0 and
+// t = 1/(1 + x/2), erfc(x) = t exp(-x^2 - 1.26551223 + t(1.00002368 + ...)),
+// relative error below 1.2e-7.  Here x = |z| / sqrt 2, so t = 1/(1 + |z|/(2 sqrt 2))
+// and -x^2 = -z^2 / 2; the exponential is taken in base 2 with log2(e) folded
+// into the fit's coefficients and the factor 1/2 of h folded into its
+// constant term (minus 1 in the exponent): h = t * 2^(C(t) - z^2 log2(e) / 2),
+// C_i = log2(e) c_i (C_0 = log2(e) c_0 - 1).  15 vector instructions and two
+// transcendentals per element.
 __device__ __forceinline__ float gelu_erf(float z)
 {
-    return 0.5f * z * erfc_cheb(-z * 0.70710678118654752f);
+    const float a = fabsf(z);
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(a, 0.35355338f, 1.0f));
+    float p = 0.24651730f;
+    p = __builtin_fmaf(p, t, -1.18611491f);
+    p = __builtin_fmaf(p, t, 2.14747453f);
+    p = __builtin_fmaf(p, t, -1.63775313f);
+    p = __builtin_fmaf(p, t, 0.40232158f);
+    p = __builtin_fmaf(p, t, -0.26875687f);
+    p = __builtin_fmaf(p, t, 0.13963005f);
+    p = __builtin_fmaf(p, t, 0.53970063f);
+    p = __builtin_fmaf(p, t, 1.44272923f);
+    p = __builtin_fmaf(p, t, -2.82574821f);
+    const float h = t * __builtin_amdgcn_exp2f(__builtin_fmaf(z * -0.72134751f, z, p));
+    return __builtin_fmaf(-a, h, fmaxf(z, 0.0f));
 }
 
 // Apply chain operators FIRST..LAST (1 = bias, 2 = gelu, 3 = residual).
