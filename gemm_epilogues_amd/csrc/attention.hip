@@ -267,6 +267,20 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         });
         __builtin_amdgcn_sched_barrier(0);
 
+        // V^T fragments of key block kk (16 keys) into vr; the first block's
+        // reads go out now, under the softmax
+        auto read_v = [&](auto kkc, u32x2 (&vr)[4][2]) __attribute__((always_inline)) {
+            constexpr int kk = decltype(kkc)::value;
+            constexpr int VOFF = SOFF + (32 * (kk >> 1) + 16 * (kk & 1)) * att::ROWB;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                vr[mt][0] = att_read_tr16<VOFF>(va[mt][0]);
+                vr[mt][1] = att_read_tr16<VOFF>(va[mt][1]);
+            }
+        };
+        u32x2 vbuf[2][4][2];
+        read_v(std::integral_constant<int, 0>{}, vbuf[0]);
+
         // ---- online softmax: lane holds query `query`, keys kt*64 + 32 t + 8 (r/4) + 4 hl + r%4.
         // Raw scores are masked and maximised (a positive scale keeps the
         // order); the scale enters once, fused into each exponent's argument.
@@ -323,22 +337,23 @@ __global__ __launch_bounds__(att::NT, 2) void attention_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- O^T += V^T P^T over the tile's keys (4 k-steps x 4 d-tiles)
+        // ---- O^T += V^T P^T over the tile's keys (4 k-steps x 4 d-tiles); the
+        // V^T fragments of k-step kk+1 are read while those of kk feed the MFMAs
         att_static_for<0, 4>([&](auto kkc) {
-            constexpr int kk = decltype(kkc)::value, t = kk >> 1, h = kk & 1;
-            constexpr int VOFF = SOFF + (32 * t + 16 * h) * att::ROWB;
-            u32x2 vr[4][2];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                vr[mt][0] = att_read_tr16<VOFF>(va[mt][0]);
-                vr[mt][1] = att_read_tr16<VOFF>(va[mt][1]);
+            constexpr int kk = decltype(kkc)::value, t = kk >> 1, h = kk & 1, cb = kk & 1;
+            if constexpr (kk < 3) {
+                read_v(std::integral_constant<int, kk + 1>{}, vbuf[cb ^ 1]);
+                asm volatile("s_waitcnt lgkmcnt(8)"
+                             : "+v"(vbuf[cb][0][0]), "+v"(vbuf[cb][0][1]), "+v"(vbuf[cb][1][0]), "+v"(vbuf[cb][1][1]),
+                               "+v"(vbuf[cb][2][0]), "+v"(vbuf[cb][2][1]), "+v"(vbuf[cb][3][0]), "+v"(vbuf[cb][3][1]));
+            } else {
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(vbuf[cb][0][0]), "+v"(vbuf[cb][0][1]), "+v"(vbuf[cb][1][0]), "+v"(vbuf[cb][1][1]),
+                               "+v"(vbuf[cb][2][0]), "+v"(vbuf[cb][2][1]), "+v"(vbuf[cb][3][0]), "+v"(vbuf[cb][3][1]));
             }
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(vr[0][0]), "+v"(vr[0][1]), "+v"(vr[1][0]), "+v"(vr[1][1]),
-                           "+v"(vr[2][0]), "+v"(vr[2][1]), "+v"(vr[3][0]), "+v"(vr[3][1]));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const u32x4 av = {vr[mt][0].x, vr[mt][0].y, vr[mt][1].x, vr[mt][1].y};
+                const u32x4 av = {vbuf[cb][mt][0].x, vbuf[cb][mt][0].y, vbuf[cb][mt][1].x, vbuf[cb][mt][1].y};
                 oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                    __builtin_bit_cast(bf16x8, pf[t][h]), oacc[mt],
                                                                    0, 0, 0);
