@@ -124,3 +124,35 @@ def test_many_short_heads():
     ref = oracle.causal_attention_f64(Q, K, V, SCALE)
     ok, worst = check(out, ref, colmax_prefix(V))
     assert ok, worst
+
+
+@pytest.mark.parametrize("case", ["wide_random", "rising_ramp"])
+def test_wide_dynamic_range(case):
+    """Scores far outside the configuration's spread, so the running reference
+    the kernel subtracts in the exponents moves often and by large steps:
+    scale 1 on N(0, 4) queries and keys (scaled scores of spread ~23, i.e.
+    ~33 in base 2); and a ramp whose scores rise by just under 8 (base 2) per
+    64-key tile, so the reference trails the max by nearly the full slack
+    before each move.  Same bar as everywhere else; no inf or NaN."""
+    BH, S = 2, 300
+    announce(f"attention wide dynamic range ({case})")
+    Q, K, V = synth.attention_inputs(BH, S, 128, salt=51)
+    if case == "wide_random":
+        scale = 1.0
+        Q = synth.f32_to_bf16_bits((2.0 * vals(Q)).astype(np.float32))
+        K = synth.f32_to_bf16_bits((2.0 * vals(K)).astype(np.float32))
+    else:
+        scale = 1.0
+        step = 7.9 / 64 / np.log2(np.e)          # natural-log rise per key: 7.9 in base 2 per tile
+        q = np.zeros((BH, S, 128))
+        q[:, :, 0] = 1.0
+        k = np.zeros((BH, S, 128))
+        k[:, :, 0] = step * np.arange(S)[None, :]
+        k[:, :, 1:] = 0.25 * vals(K)[:, :, 1:]
+        Q = synth.f32_to_bf16_bits(q.astype(np.float32))
+        K = synth.f32_to_bf16_bits(k.astype(np.float32))
+    out = run(Q, K, V, scale)
+    assert np.all(np.isfinite(vals(out)))
+    ref = oracle.causal_attention_f64(Q, K, V, scale)
+    ok, worst = check(out, ref, colmax_prefix(V))
+    assert ok, worst
