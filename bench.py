@@ -843,19 +843,44 @@ def main():
                                    "TFLOPs": round(flops_ps / 1e12, 1), "flops_source": p_src,
                                    "launch_us": model_rows["launch_us"],
                                    "register_rule": "512 live registers per lane (one wave per SIMD), x3 beyond"}}
-            for shape, (M, N, K) in (("decode", DECODE_MNK), ("gemm", GEMM_MNK)):
-                st = fc.fc_gemm_epilogue_stages(M, N, K)
-                rows = {}
-                for (sh, plan), t in meas.items():
-                    if sh != shape:
-                        continue
-                    pred = fc.fc_segments_time(st, list(plan), 2, m)
-                    rows["".join(map(str, plan))] = {"measured_us": round(t * 1e6, 2), "model_us": round(pred * 1e6, 2),
-                                                     "model_over_measured": round(pred / t, 3)}
-                if rows:
-                    best_model, _ = fc.fc_best_split(st, 2, m)
-                    best_meas = min(((t, p) for (sh, p), t in meas.items() if sh == shape))[1]
-                    val[shape] = {"plans": rows, "model_best": best_model, "measured_best": list(best_meas)}
+
+            def validate(model):
+                res = {}
+                for shape, (M, N, K) in (("decode", DECODE_MNK), ("gemm", GEMM_MNK)):
+                    st = fc.fc_gemm_epilogue_stages(M, N, K)
+                    rows = {}
+                    for (sh, plan), t in meas.items():
+                        if sh != shape:
+                            continue
+                        pred = fc.fc_segments_time(st, list(plan), 2, model)
+                        rows["".join(map(str, plan))] = {"measured_us": round(t * 1e6, 2),
+                                                         "model_us": round(pred * 1e6, 2),
+                                                         "model_over_measured": round(pred / t, 3)}
+                    if rows:
+                        best_model, _ = fc.fc_best_split(st, 2, model)
+                        best_meas = min(((t, p) for (sh, p), t in meas.items() if sh == shape))[1]
+                        res[shape] = {"plans": rows, "model_best": best_model, "measured_best": list(best_meas)}
+                return res
+            val.update(validate(m))
+            # The same model with the register rule replaced by the occupancy steps the fat
+            # probe measures on this device: (live registers, time / time at the fewest
+            # registers) for every unspilled point, the spilled point's ratio beyond them.
+            sweep = model_rows.get("fat_sweep_K4", {}).get("rows", [])
+            base = next((r["us"] for r in sweep if r["T"] == 0), None)
+            pts = sorted((r["vgprs"] + r["agprs"], r["us"] / base) for r in sweep
+                         if base and r["scratch_bytes_per_lane"] == 0)
+            spilled = [r["us"] / base for r in sweep if base and r["scratch_bytes_per_lane"] > 0]
+            if pts and spilled:
+                levels, fmax = [], 0.0
+                for regs, f in pts:                  # strictly increasing levels, non-decreasing factors
+                    fmax = max(fmax, f)
+                    if not levels or regs > levels[-1][0]:
+                        levels.append((regs, round(fmax, 3)))
+                mo = fc.cost_model(hbm * 1e9, flops_ps, launch_s, levels=tuple(levels[:8]),
+                                   spill_factor=round(max(spilled[0], fmax), 3))
+                val["occupancy_rule"] = {"levels": levels[:8], "spill_factor": round(max(spilled[0], fmax), 3),
+                                         "source": "fat probe sweep (K = 4): time over the T = 0 point",
+                                         **validate(mo)}
             model_rows["validation"] = val
         comp["cost_model"] = model_rows
 
