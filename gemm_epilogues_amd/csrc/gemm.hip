@@ -7,12 +7,19 @@
 // single fp16 store.  Later segments: pointwise kernels over the fp16 [M,N]
 // intermediate (128-bit loads/stores).
 //
-// GEMM data flow: A [M,K] and B [K,N] are row-major.  Each workgroup owns a
-// BM x BN output tile; K advances in BK slabs through a two-stage LDS ring.
-// A slabs are copied as-is (k contiguous).  B slabs are loaded as 8x8 fp16
-// blocks, transposed in registers and stored n-major, so both MFMA operands
-// are read from LDS as 16-byte k-contiguous fragments.  Rows of LDS are padded
-// by 16 bytes, which spreads the 16-byte fragment reads across all banks.
+// Kernels, by shape: large problems (>= 128 tiles of 256x256, K % 64 == 0) run
+// gemm_ring_kernel (loads straight into a 4-stage LDS ring, B fragments by the
+// transposing LDS read; see its own comment); M <= 16 runs the split-K
+// gemm_decode_kernel; the rest run register-staged kernels (gemm_big_kernel,
+// gemm_epi_kernel) and, for tiny M without a decode split, gemm_skinny_kernel.
+//
+// Register-staged data flow: A [M,K] and B [K,N] are row-major.  Each
+// workgroup owns a BM x BN output tile; K advances in BK slabs through a
+// two-stage LDS ring.  A slabs are copied as-is (k contiguous).  B slabs are
+// loaded as 8x8 fp16 blocks, transposed in registers and stored n-major, so
+// both MFMA operands are read from LDS as 16-byte k-contiguous fragments.
+// Rows of LDS are padded by 16 bytes, which spreads the 16-byte fragment reads
+// across all banks.
 #include "fc_internal.h"
 
 #include <type_traits>
