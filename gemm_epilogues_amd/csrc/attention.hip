@@ -6,8 +6,11 @@
 //
 // Layout: Q, K, V, O bf16 [BH, S, 128] row-major.  A workgroup owns 128
 // queries of one head (4 waves x 32); 64-key tiles of K and V are loaded
-// into a double-buffered LDS ring (2 x (16 + 16) KiB) with direct-to-LDS
-// loads, one tile ahead.  Per tile each wave computes
+// into a double-buffered LDS ring (2 x (16 + 16) KiB) one tile ahead, by
+// buffer loads that write LDS directly (the tile's row offset rides in the
+// scalar offset, so the per-lane addresses are computed once); only a ragged
+// last tile goes through clamped per-lane global loads.  Per tile each wave
+// computes
 //   S^T = K Q^T           (v_mfma_f32_32x32x16_bf16, K from LDS as the A
 //                          operand, Q fragments held in registers)
 // so a lane owns one query and 32 of the tile's 64 keys (the other 32 are in
