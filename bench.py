@@ -428,8 +428,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the hot path is single-device "
-              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: every kernel of the hot path works on one "
+              "device's share of the data; sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -117,7 +117,7 @@ MUTANTS = [
      "        out.append(plan)", "test_oracle_ledger.py"),
 ]
 
-BASELINE_PINS = sorted({m[4] for m in MUTANTS})
+UNCHANGED_PINS = sorted({m[4] for m in MUTANTS})
 
 
 def _copy_oracle(dst_root, fname=None, old=None, new=None):
@@ -158,7 +158,7 @@ def outcomes(tmp_path_factory):
     jobs = {}
     base = str(tmp_path_factory.mktemp("oracle_unchanged"))
     _copy_oracle(base)
-    jobs[None] = (base, BASELINE_PINS)
+    jobs[None] = (base, UNCHANGED_PINS)
     for mid, fname, old, new, pins in MUTANTS:
         d = str(tmp_path_factory.mktemp(mid))
         _copy_oracle(d, fname, old, new)
