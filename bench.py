@@ -200,7 +200,6 @@ def measure_model_rows(torch, stream, groups, bufs, fc):
     a t(n) = a + b n fit of plain copies, the fat probe's register sweep, and
     every split plan of both GEMM shapes (eager, and for the decode shape also
     replayed from a captured HIP graph)."""
-    import json as _json
     from gemm_epilogues_amd import envelope as env
     dev = torch.device("cuda", 0)
     out = {}
@@ -227,8 +226,6 @@ def measure_model_rows(torch, stream, groups, bufs, fc):
     if "chain" in groups:
         sets, coef = bufs["chain"]
         a4, b4 = synth_chain_coef(4)
-        res_path = os.path.join(ROOT, "gemm_epilogues_amd", "kernel_resources.json")
-        res = _json.load(open(res_path)) if os.path.exists(res_path) else {}
         sweep = []
         t_fused = _median_ms(torch, stream, lambda r: fc.fc_chain(sets[r][0], sets[r][1], a4, b4, True,
                                                                      fc.FC_CHAIN_FUSED), CHAIN_SETS)
@@ -237,12 +234,10 @@ def measure_model_rows(torch, stream, groups, bufs, fc):
                              device=dev)
             t = _median_ms(torch, stream, lambda r, T=T, sk=sk: fc.fc_chain(sets[r][0], sets[r][1], a4, b4, True,
                                                                              fc.FC_CHAIN_FAT, sk, T), CHAIN_SETS)
-            key = [k for k in res if "chain_fat_kernel" in k and f"ILi4ELb1ELi{T}E" in k]
-            r = res[key[0]] if key else {}
+            r = fc.fc_kernel_info(f"fc::chain_fat_kernel<4, true, {T}>")
             sweep.append({"T": T, "us": round(t * 1e3, 2), "over_fused": round(t / t_fused, 2),
-                          "vgprs": r.get("VGPRs"), "agprs": r.get("AGPRs"),
-                          "waves_per_simd": r.get("Occupancy [waves/SIMD]"),
-                          "scratch_bytes_per_lane": r.get("ScratchSize [bytes/lane]")})
+                          "vgprs": r["vgprs"], "agprs": r["agprs"], "waves_per_simd": r["waves_per_simd"],
+                          "scratch_bytes_per_lane": r["scratch_bytes"]})
         out["fat_sweep_K4"] = {"fused_us": round(t_fused * 1e3, 2), "rows": sweep}
     plans_all = [[4], [3, 1], [1, 3], [2, 2], [2, 1, 1], [1, 2, 1], [1, 1, 2], [1, 1, 1, 1]]
     meas = {}

@@ -113,6 +113,8 @@ _SIGS = {
     "fc_segments_time": (ctypes.c_double, [_P, _I, _P, _I, _I, _P]),
     "fc_best_split": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "fc_gemm_epilogue_stages": (_I, [_I64, _I64, _I64, _P]),
+    "fc_kernel_info": (_I, [ctypes.c_char_p] + [ctypes.POINTER(_I)] * 6),
+    "fc_kernel_name": (ctypes.c_char_p, [_I]),
     "fc_status_string": (ctypes.c_char_p, [_I]),
     "fc_version": (ctypes.c_char_p, []),
 }
@@ -450,3 +452,26 @@ def fc_chain_bytes(n: int, K: int, mode: int) -> int:
 
 def fc_softmax_bytes(BH: int, S: int, tile: int, mode: int) -> int:
     return int(_lib.fc_softmax_bytes(int(BH), int(S), int(tile), int(mode)))
+
+
+# ---------------------------------------------------------------- kernel resources (host only)
+
+KERNEL_INFO_FIELDS = ("vgprs", "agprs", "sgprs", "lds_bytes", "scratch_bytes", "waves_per_simd")
+
+
+def fc_kernel_info(name: str) -> dict:
+    """Compiler resource report of one kernel of the library, by demangled name."""
+    vals = [ctypes.c_int(-1) for _ in KERNEL_INFO_FIELDS]
+    _check(_lib.fc_kernel_info(name.encode(), *[ctypes.byref(v) for v in vals]), f"fc_kernel_info({name!r})")
+    return {f: v.value for f, v in zip(KERNEL_INFO_FIELDS, vals)}
+
+
+def fc_kernel_names() -> list:
+    """Every kernel name fc_kernel_info accepts, in table order."""
+    out, i = [], 0
+    while True:
+        n = _lib.fc_kernel_name(i)
+        if n is None:
+            return out
+        out.append(n.decode())
+        i += 1

@@ -4,6 +4,9 @@
 #include <stddef.h>
 
 #include "../../include/fc.h"
+#include "kernel_info.h"
+
+#include <string.h>
 
 namespace {
 
@@ -201,3 +204,31 @@ extern "C" const char *fc_status_string(int status)
 }
 
 extern "C" const char *fc_version(void) { return "fc 0.1.0 gfx950"; }
+
+// Register and LDS use per kernel, the quantities behind the occupancy side of
+// fusion ("C-05. Kernel Fusion 代价边界", section 2: every live value a fused
+// kernel keeps costs registers per thread, and more registers per thread
+// means fewer resident waves).  Served from the table build.py writes from
+// the compiler's resource report of this build.
+extern "C" int fc_kernel_info(const char *name, int *vgprs, int *agprs, int *sgprs, int *lds_bytes,
+                              int *scratch_bytes, int *waves_per_simd)
+{
+    if (!name) return FC_ERR_NULL;
+    for (int i = 0; i < fc::kKernelInfoCount; ++i) {
+        const fc::KernelInfoRow &r = fc::kKernelInfo[i];
+        if (strcmp(r.name, name) != 0) continue;
+        if (vgprs) *vgprs = r.vgprs;
+        if (agprs) *agprs = r.agprs;
+        if (sgprs) *sgprs = r.sgprs;
+        if (lds_bytes) *lds_bytes = r.lds_bytes;
+        if (scratch_bytes) *scratch_bytes = r.scratch_bytes;
+        if (waves_per_simd) *waves_per_simd = r.waves_per_simd;
+        return FC_OK;
+    }
+    return FC_ERR_UNSUPPORTED;
+}
+
+extern "C" const char *fc_kernel_name(int i)
+{
+    return (i >= 0 && i < fc::kKernelInfoCount) ? fc::kKernelInfo[i].name : nullptr;
+}

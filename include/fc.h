@@ -323,6 +323,32 @@ int fc_best_split(const fc_stage *stages, int n_stages, int elem_bytes, const fc
 /* The four stages of the GEMM epilogue chain for (M, N, K) into out[4]. */
 int fc_gemm_epilogue_stages(int64_t M, int64_t N, int64_t K, fc_stage *out);
 
+/* ------------------------------------------------------ kernel resources */
+
+/*
+ * fc_kernel_info -- registers and LDS of one kernel of this library as built,
+ * the quantities that set occupancy ("C-05. Kernel Fusion 代价边界", section 2:
+ * a fused kernel pays for every value it keeps live in registers per thread,
+ * and fewer resident waves follow).  Values come from the compiler's resource
+ * report of this build, compiled into the library: vector registers (VGPRs),
+ * accumulation registers (AGPRs), scalar registers, static LDS bytes per
+ * workgroup, scratch bytes per lane (non-zero means spills) and the waves per
+ * SIMD the register and LDS use allow.
+ *
+ *  name     the kernel's demangled name without its parameter list, e.g.
+ *           "fc::attention_fwd_kernel" or "fc::chain_fat_kernel<4, true, 48>";
+ *           fc_kernel_name() lists every name.
+ *  outputs  host ints; any of them may be NULL.
+ * Host only: never touches the device.  Returns FC_OK, FC_ERR_NULL (name is
+ * NULL) or FC_ERR_UNSUPPORTED (no kernel of that name).
+ */
+int fc_kernel_info(const char *name, int *vgprs, int *agprs, int *sgprs, int *lds_bytes,
+                   int *scratch_bytes, int *waves_per_simd);
+
+/* Name of kernel i (0-based, sorted by name) for fc_kernel_info, or NULL when
+ * i is out of range.  The string is static. */
+const char *fc_kernel_name(int i);
+
 /* Static text for a status code. */
 const char *fc_status_string(int status);
 

@@ -295,3 +295,65 @@ def test_rmsnorm_accounting_and_validation():
     assert L.fc_rmsnorm(MIS, FAKE + big, FAKE + 2 * big, 4, 64, 1e-5, 0, None, 0, None) == fc.FC_ERR_ALIGN
     assert L.fc_rmsnorm(FAKE, FAKE + big, FAKE + 512, 4, 64, 1e-5, 0, None, 0, None) == fc.FC_ERR_ALIAS
     assert L.fc_rmsnorm(*args, 4, 64, 1e-5, 1, None, 0, None) == fc.FC_ERR_WORKSPACE
+
+
+def _report_by_plain_name():
+    """kernel_resources.json (the compiler's report, keyed by mangled name) keyed
+    by demangled name without the parameter list, for the library's kernels."""
+    import subprocess
+    path = os.path.join(os.path.dirname(fc.__file__), "kernel_resources.json")
+    with open(path) as f:
+        rep = __import__("json").load(f)
+    mangled = sorted(rep)
+    plain = subprocess.run(["c++filt"], input="\n".join(mangled), capture_output=True, text=True,
+                           check=True).stdout.splitlines()
+    out = {}
+    for m, full in zip(mangled, plain):
+        full = full[5:] if full.startswith("void ") else full
+        depth, cut = 0, len(full)
+        for i, ch in enumerate(full):
+            depth += (ch == "<") - (ch == ">")
+            if ch == "(" and depth == 0:
+                cut = i
+                break
+        out[full[:cut]] = rep[m]
+    return out
+
+
+def test_kernel_info_matches_the_compiler_report():
+    names = fc.fc_kernel_names()
+    assert len(names) == len(set(names)) and names == sorted(names)
+    rep = _report_by_plain_name()
+    fields = {"vgprs": "VGPRs", "agprs": "AGPRs", "sgprs": "TotalSGPRs", "lds_bytes": "LDS Size [bytes/block]",
+              "scratch_bytes": "ScratchSize [bytes/lane]", "waves_per_simd": "Occupancy [waves/SIMD]"}
+    for n in names:
+        info = fc.fc_kernel_info(n)
+        assert {k: info[k] for k in fields} == {k: rep[n][v] for k, v in fields.items()}, n
+    # every product kernel is listed; the measurement probes (a separate library) are not
+    for key in ("fc::attention_fwd_kernel", "fc::gemm_ring_kernel<3>", "fc::gemm_decode_kernel<3>",
+                "fc::chain_fused_kernel<4, true>", "fc::chain_fat_kernel<4, true, 48>", "fc::rmsnorm_fused_kernel<4>"):
+        assert key in names, key
+    assert not any(n.startswith("fc::fce_") or "envelope" in n for n in names)
+
+
+def test_kernel_info_shows_the_register_cliff():
+    # the fused chain keeps few values live and runs at full occupancy; the fat
+    # probe's 48 live fp32x4 temporaries push the registers past 192 and the
+    # occupancy down to 2 waves per SIMD, without spilling
+    fused = fc.fc_kernel_info("fc::chain_fused_kernel<4, true>")
+    fat = fc.fc_kernel_info("fc::chain_fat_kernel<4, true, 48>")
+    assert fused["waves_per_simd"] == 8 and fused["scratch_bytes"] == 0
+    assert fat["vgprs"] + fat["agprs"] >= 192 and fat["waves_per_simd"] <= 2 and fat["scratch_bytes"] == 0
+    att = fc.fc_kernel_info("fc::attention_fwd_kernel")
+    assert att["lds_bytes"] == 65536 and att["waves_per_simd"] == 2 and att["scratch_bytes"] == 0
+
+
+def test_kernel_info_errors():
+    assert fc.lib().fc_kernel_info(None, None, None, None, None, None, None) == fc.FC_ERR_NULL
+    assert fc.lib().fc_kernel_info(b"fc::no_such_kernel", None, None, None, None, None, None) == \
+        fc.FC_ERR_UNSUPPORTED
+    with pytest.raises(fc.FcError):
+        fc.fc_kernel_info("attention_fwd_kernel")             # the namespace is part of the name
+    assert fc.lib().fc_kernel_info(b"fc::attention_fwd_kernel", None, None, None, None, None, None) == fc.FC_OK
+    assert fc.lib().fc_kernel_name(-1) is None
+    assert fc.lib().fc_kernel_name(len(fc.fc_kernel_names())) is None
