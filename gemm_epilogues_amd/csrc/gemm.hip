@@ -9,9 +9,10 @@
 //
 // Kernels, by shape: large problems (>= 128 tiles of 256x256, K % 64 == 0) run
 // gemm_ring_kernel (loads straight into a 4-stage LDS ring, B fragments by the
-// transposing LDS read; see its own comment); M <= 16 runs the split-K
-// gemm_decode_kernel; the rest run register-staged kernels (gemm_big_kernel,
-// gemm_epi_kernel) and, for tiny M without a decode split, gemm_skinny_kernel.
+// transposing LDS read; see its own comment); M <= 64 with N % 64 == 0 and
+// K % 256 == 0 runs the split-K gemm_decode_kernel; the rest run
+// register-staged kernels (gemm_big_kernel, gemm_epi_kernel) and, for M <= 16
+// without a decode split, gemm_skinny_kernel.
 //
 // Register-staged data flow: A [M,K] and B [K,N] are row-major.  Each
 // workgroup owns a BM x BN output tile; K advances in BK slabs through a
@@ -821,9 +822,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     }
 }
 
-// ------------------------------------------------------------------ decode GEMM (M <= 16, split K)
+// ------------------------------------------------------------------ decode GEMM (M <= 64, split K)
 
-// At M <= 16 the GEMM is a stream over B (K x N fp16), so the layout is
+// At M <= 64 the GEMM is a stream over B (K x N fp16), so the layout is
 // chosen for the stream: every workgroup owns a 64-column strip of B (one
 // full 128-byte line per k-row) and a 1/P share of K, and requests its whole
 // slab (at most 1024 k-rows, 128 KiB) at once with direct-to-LDS loads; its 8
@@ -831,17 +832,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 // loaded, so no barrier sits between the loads and the MFMAs.  B slab layout
 // per wave: k-row k at 128 k bytes, 16-byte unit u at u ^ dec_swz(k), which
 // spreads the transposing reads (ds_read_b64_tr_b16, four k-rows per
-// 16-lane group) over all banks.  A fragments (16 rows x the wave's k-range)
-// go straight to registers.  One v_mfma_f32_16x16x32_f16 per 32-deep k-step
-// and 16-column tile.
+// 16-lane group) over all banks.  A fragments (MB blocks of 16 rows x the
+// wave's k-range) go straight to registers.  Per 32-deep k-step and 16-column
+// tile, one B fragment read feeds one v_mfma_f32_16x16x32_f16 per row block,
+// so B leaves LDS once whatever M is.
 //
-// The eight wave partials are summed through LDS in wave order.  With P = 1
-// the workgroup applies the epilogue and stores Y.  With P > 1 it publishes its
-// 16x64 fp32 partial to the workspace and takes a ticket from the strip's
-// arrival counter; the workgroup that draws the last ticket sums the P
-// partials in split order (so the result does not depend on arrival order),
-// applies the epilogue, stores Y and puts the counter back to zero.  No
-// workgroup ever waits for another, so the launch needs no co-residency.
+// The eight wave partials are summed through LDS in wave order, one 16-row
+// block at a time.  With P = 1 the workgroup applies the epilogue and stores
+// Y.  With P > 1 it publishes its MB x 16 x 64 fp32 partial to the workspace
+// and takes a ticket from the strip's arrival counter; the workgroup that
+// draws the last ticket sums the P partials in split order (so the result
+// does not depend on arrival order), applies the epilogue, stores Y and puts
+// the counter back to zero.  No workgroup ever waits for another, so the
+// launch needs no co-residency.
 //
 // Visibility across XCDs without a full L2 write-back: partials are written
 // with device-scope stores (they write through to the device coherence point
@@ -850,10 +853,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 // workgroup reads the partials with device-scope loads, which are served from
 // the coherence point rather than a possibly stale line of its own XCD's L2.
 namespace dec {
-constexpr int WAVES = 8, NT = WAVES * 64, W = 64, ROW = W * 2, KSTEP = 32, MAXSTEPS = 4;
-constexpr int TILE = 16 * W;                                     // outputs per strip
+constexpr int WAVES = 8, NT = WAVES * 64, W = 64, ROW = W * 2, KSTEP = 32;
+constexpr int TILE = 16 * W;                                     // outputs per strip and 16-row block
+constexpr int MAXMB = 4;                                         // 16-row blocks: M <= 64
 constexpr int MAXP = 64;
-constexpr int MAX_LDS = WAVES * KSTEP * MAXSTEPS * ROW;          // 128 KiB
+// k-steps a wave may hold (its A fragments stay in registers): 4 up to 32
+// rows, 2 at 64 rows, keeping the kernel within 128 VGPRs (4 waves per SIMD)
+__host__ __device__ constexpr int max_steps(int mb) { return mb <= 2 ? 4 : 2; }
+constexpr int MAX_LDS = WAVES * KSTEP * 4 * ROW;                 // 128 KiB
 }
 
 __device__ __forceinline__ int dec_swz(int k) { return 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1); }
@@ -869,12 +876,13 @@ __device__ __forceinline__ void dec_store_pair(uint16_t *__restrict__ out, int N
                    apply_ops<OP_BIAS, LAST>(v1, f16_hi(bw), f16_hi(rw)));
 }
 
-template <int LAST>
+template <int LAST, int MB>
 __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
     int M, int N, int K, int P, uint32_t *__restrict__ counters, float *__restrict__ partials)
 {
+    constexpr int MS = dec::max_steps(MB);
     extern __shared__ __attribute__((aligned(1024))) char dec_lds[];
     __shared__ int is_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -893,20 +901,29 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
     const uint32_t slab0 = (uint32_t)(uintptr_t)slab;
     const int g = lane >> 4, i = lane & 15;
 
-    // the output pair this thread stores if its workgroup finishes the strip:
-    // bias and R are fetched now, off the critical tail
-    const int e = 2 * threadIdx.x, row = e / dec::W, col = n0 + e % dec::W;
-    uint32_t bw = 0u, rw = 0u;
+    // the output pairs this thread stores if its workgroup finishes the strip
+    // (row 16 rb + e / 64 of each row block rb): bias and R are fetched now,
+    // off the critical tail
+    const int e = 2 * threadIdx.x, erow = e / dec::W, col = n0 + e % dec::W;
+    uint32_t bw = 0u, rw[MB];
     if (LAST >= OP_BIAS) bw = *reinterpret_cast<const uint32_t *>(bias + col);
-    if (LAST >= OP_RES && row < M) rw = *reinterpret_cast<const uint32_t *>(R + (int64_t)row * N + col);
-
-    // A fragments (16x16x32 A operand: row i, k = 8g .. 8g+7 of each k-step);
-    // rows past M repeat row M-1 and are never stored.
-    f16x8 afr[dec::MAXSTEPS];
-    const uint16_t *arow = A + (int64_t)min(i, M - 1) * K + kbase + 8 * g;
 #pragma unroll
-    for (int t = 0; t < dec::MAXSTEPS; ++t)
-        afr[t] = *reinterpret_cast<const f16x8 *>(arow + min(t, nsteps - 1) * dec::KSTEP);
+    for (int rb = 0; rb < MB; ++rb) {
+        rw[rb] = 0u;
+        const int row = 16 * rb + erow;
+        if (LAST >= OP_RES && row < M) rw[rb] = *reinterpret_cast<const uint32_t *>(R + (int64_t)row * N + col);
+    }
+
+    // A fragments (16x16x32 A operand: row 16 rb + i, k = 8g .. 8g+7 of each
+    // k-step); rows past M repeat row M-1 and are never stored.
+    f16x8 afr[MB][MS];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+        const uint16_t *arow = A + (int64_t)min(16 * rb + i, M - 1) * K + kbase + 8 * g;
+#pragma unroll
+        for (int t = 0; t < MS; ++t)
+            afr[rb][t] = *reinterpret_cast<const f16x8 *>(arow + min(t, nsteps - 1) * dec::KSTEP);
+    }
     // B slab: each instruction moves 8 k-rows (1 KiB); lane l lands at byte
     // 16 l, i.e. row l / 8, unit l % 8, so it fetches the unit that the
     // swizzle places there.
@@ -922,11 +939,13 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0xF70);                            // vmcnt(0): slab and A landed
 
-    f32x4 acc[4];
+    f32x4 acc[MB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-    for (int t = 0; t < dec::MAXSTEPS; ++t) {
+        for (int j = 0; j < 4; ++j) acc[rb][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
         if (t < nsteps) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -941,36 +960,48 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
                                            16 * ((2 * j + ((i & 3) >> 1)) ^ dec_swz(k)) + (i & 1) * 8);
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bh[0]), "+v"(bh[1]));
-                const u32x4 bw = {bh[0].x, bh[0].y, bh[1].x, bh[1].y};
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[t], __builtin_bit_cast(f16x8, bw), acc[j],
-                                                                0, 0, 0);
+                const u32x4 bq = {bh[0].x, bh[0].y, bh[1].x, bh[1].y};
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb)
+                    acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[rb][t], __builtin_bit_cast(f16x8, bq),
+                                                                        acc[rb][j], 0, 0, 0);
             }
         }
     }
-    __syncthreads();                                              // every wave done with its slab
-    // 16x16 result layout: lane holds column 16j + i, rows 4g + r
+    // 16x16 result layout: lane holds column 16j + i, rows 4g + r.  Each
+    // thread owns the output pair e, e+1 of every 16x64 row block.
     float *part = (float *)dec_lds;
+    float v0[MB], v1[MB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int rb = 0; rb < MB; ++rb) {
+        __syncthreads();                                          // slab (or previous block) consumed
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[wave * dec::TILE + (4 * g + r) * dec::W + 16 * j + i] = acc[j][r];
-    __syncthreads();
-
-    // each thread owns the output pair e, e+1 of the 16x64 strip tile
-    float v0 = 0.0f, v1 = 0.0f;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int w = 0; w < dec::WAVES; ++w) {
-        const float2 pv = *reinterpret_cast<const float2 *>(part + w * dec::TILE + e);
-        v0 += pv.x;
-        v1 += pv.y;
+            for (int r = 0; r < 4; ++r) part[wave * dec::TILE + (4 * g + r) * dec::W + 16 * j + i] = acc[rb][j][r];
+        __syncthreads();
+        v0[rb] = 0.0f;
+        v1[rb] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < dec::WAVES; ++w) {
+            const float2 pv = *reinterpret_cast<const float2 *>(part + w * dec::TILE + e);
+            v0[rb] += pv.x;
+            v1[rb] += pv.y;
+        }
     }
     if (P == 1) {
-        if (row < M) dec_store_pair<LAST>(out, N, row, col, bw, rw, v0, v1);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+            if (16 * rb + erow < M) dec_store_pair<LAST>(out, N, 16 * rb + erow, col, bw, rw[rb], v0[rb], v1[rb]);
         return;
     }
-    uint64_t *mine = reinterpret_cast<uint64_t *>(partials + ((int64_t)strip * P + split) * dec::TILE + e);
-    __hip_atomic_store(mine, __builtin_bit_cast(uint64_t, make_float2(v0, v1)), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    // partials: [strip][split][row block][16 x 64]
+    const int64_t pbase = ((int64_t)strip * P + split) * MB * dec::TILE + e;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(partials + pbase + rb * dec::TILE),
+                           __builtin_bit_cast(uint64_t, make_float2(v0[rb], v1[rb])), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0xF70);                            // vmcnt(0): the partial is at the coherence point
     __syncthreads();
     if (threadIdx.x == 0)
@@ -978,41 +1009,53 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
                   (uint32_t)(P - 1);
     __syncthreads();
     if (!is_last) return;
-    // the P partials, eight loads in flight at a time, summed in split order
-    float s0 = 0.0f, s1 = 0.0f;
-    const uint64_t *src = reinterpret_cast<const uint64_t *>(partials + (int64_t)strip * P * dec::TILE + e);
-    for (int p0 = 0; p0 < P; p0 += 8) {
-        uint64_t w[8];
+    // the P partials of each row block, eight loads in flight at a time,
+    // summed in split order
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (p0 + q < P)
-                w[q] = __hip_atomic_load(src + (int64_t)(p0 + q) * (dec::TILE / 2), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int rb = 0; rb < MB; ++rb) {
+        float s0 = 0.0f, s1 = 0.0f;
+        const uint64_t *src =
+            reinterpret_cast<const uint64_t *>(partials + (int64_t)strip * P * MB * dec::TILE + rb * dec::TILE + e);
+        for (int p0 = 0; p0 < P; p0 += 8) {
+            uint64_t w[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (p0 + q < P) {
-                const float2 pv = __builtin_bit_cast(float2, w[q]);
-                s0 += pv.x;
-                s1 += pv.y;
-            }
+            for (int q = 0; q < 8; ++q)
+                if (p0 + q < P)
+                    w[q] = __hip_atomic_load(src + (int64_t)(p0 + q) * (MB * dec::TILE / 2), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (p0 + q < P) {
+                    const float2 pv = __builtin_bit_cast(float2, w[q]);
+                    s0 += pv.x;
+                    s1 += pv.y;
+                }
+        }
+        if (16 * rb + erow < M) dec_store_pair<LAST>(out, N, 16 * rb + erow, col, bw, rw[rb], s0, s1);
     }
-    if (row < M) dec_store_pair<LAST>(out, N, row, col, bw, rw, s0, s1);
     if (threadIdx.x == 0) __hip_atomic_store(counters + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-row blocks of the decode kernel for M rows (1, 2 or 4), 0 past 64 rows.
+static int decode_blocks(int M)
+{
+    return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 0;
 }
 
 // Split of K for the decode kernel: the smallest power of two P with at least
 // 512 workgroups (strips x P: two per CU, which streams B faster than one
 // workgroup per CU with twice the loads in flight per wave), each wave
-// holding 1..4 k-steps; else the largest P that fits.  0 when the shape does
-// not fit (then the skinny kernel runs).
+// holding 1 .. max_steps k-steps; else the largest P that fits.  0 when the
+// shape does not fit (then another kernel runs).
 static int decode_splits(int M, int N, int K)
 {
-    if (M > 16 || N % dec::W != 0 || K % (dec::WAVES * dec::KSTEP) != 0) return 0;
+    const int mb = decode_blocks(M);
+    if (mb == 0 || N % dec::W != 0 || K % (dec::WAVES * dec::KSTEP) != 0) return 0;
     const int strips = N / dec::W;
     int best = 0;
     for (int P = 1; P <= dec::MAXP; P *= 2) {
         if (K % (P * dec::WAVES * dec::KSTEP) != 0) break;
-        if (K > P * dec::WAVES * dec::KSTEP * dec::MAXSTEPS) continue;
+        if (K > P * dec::WAVES * dec::KSTEP * dec::max_steps(mb)) continue;
         best = P;
         if ((int64_t)strips * P >= 512) break;
     }
@@ -1026,7 +1069,7 @@ static size_t decode_scratch_bytes(int M, int N, int K)
     const int P = decode_splits(M, N, K);
     if (P <= 1) return 0;
     const size_t strips = (size_t)(N / dec::W);
-    return ((strips * 4 + 255) & ~(size_t)255) + strips * (size_t)P * dec::TILE * 4;
+    return ((strips * 4 + 255) & ~(size_t)255) + strips * (size_t)P * decode_blocks(M) * dec::TILE * 4;
 }
 
 // ------------------------------------------------------------------ pointwise segments
@@ -1079,21 +1122,33 @@ struct DecodeScratch {
     float *partials;
 };
 
+template <int LAST, int MB>
+static int launch_decode(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
+                         uint16_t *out, int M, int N, int K, int P, int grid, int lds, DecodeScratch ds,
+                         hipStream_t s)
+{
+    // dynamic LDS above 64 KiB has to be allowed per kernel
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)gemm_decode_kernel<LAST, MB>, hipFuncAttributeMaxDynamicSharedMemorySize, dec::MAX_LDS);
+    if (attr != hipSuccess) return FC_ERR_HIP;
+    gemm_decode_kernel<LAST, MB><<<grid, dec::NT, lds, s>>>(A, B, bias, R, out, M, N, K, P, ds.counters,
+                                                             ds.partials);
+    return launch_status();
+}
+
 template <int LAST>
 static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
                        uint16_t *out, int M, int N, int K, DecodeScratch ds, hipStream_t s)
 {
     const int P = decode_splits(M, N, K);
     if (P > 0) {
-        // dynamic LDS above 64 KiB has to be allowed per kernel
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)gemm_decode_kernel<LAST>, hipFuncAttributeMaxDynamicSharedMemorySize, dec::MAX_LDS);
-        if (attr != hipSuccess) return FC_ERR_HIP;
         const int grid = (N / dec::W) * P;
         const int lds = (K / P) * dec::ROW;
-        gemm_decode_kernel<LAST><<<grid, dec::NT, lds, s>>>(A, B, bias, R, out, M, N, K, P, ds.counters,
-                                                            ds.partials);
-        return launch_status();
+        switch (decode_blocks(M)) {
+        case 1: return launch_decode<LAST, 1>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
+        case 2: return launch_decode<LAST, 2>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
+        default: return launch_decode<LAST, 4>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
+        }
     }
     if (M <= 16) {
         gemm_skinny_kernel<kSkinnyWaves, LAST><<<(N + 15) / 16, kSkinnyWaves * 64, 0, s>>>(

@@ -86,8 +86,14 @@ def test_decode_workspace_examples():
     assert fc.fc_gemm_workspace_bytes(16, 16384, 1024, [4]) == 1024 + 256 * 2 * 4096
     # N = 32768: 512 strips fill the chip unsplit, no scratch
     assert fc.fc_gemm_workspace_bytes(16, 32768, 1024, [4]) == 0
+    # 17..32 rows: two 16-row blocks of partials; 33..64 rows: four (and at
+    # most 2 k-steps per wave, so 4096 deep needs P >= 8)
+    assert fc.fc_gemm_workspace_bytes(17, 4096, 4096, [4]) == 256 + 64 * 8 * 2 * 4096
+    assert fc.fc_gemm_workspace_bytes(32, 4096, 4096, [4]) == 256 + 64 * 8 * 2 * 4096
+    assert fc.fc_gemm_workspace_bytes(64, 4096, 4096, [4]) == 256 + 64 * 8 * 4 * 4096
+    assert fc.fc_gemm_workspace_bytes(40, 2048, 8192, [4]) == 256 + 32 * 16 * 4 * 4096
     # shapes the decode kernel does not take
-    assert fc.fc_gemm_workspace_bytes(17, 4096, 4096, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(65, 4096, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(16, 4104, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(16, 4096, 4104, [4]) == 0
 
@@ -330,7 +336,7 @@ def test_kernel_info_matches_the_compiler_report():
         info = fc.fc_kernel_info(n)
         assert {k: info[k] for k in fields} == {k: rep[n][v] for k, v in fields.items()}, n
     # every product kernel is listed; the measurement probes (a separate library) are not
-    for key in ("fc::attention_fwd_kernel", "fc::gemm_ring_kernel<3>", "fc::gemm_decode_kernel<3>",
+    for key in ("fc::attention_fwd_kernel", "fc::gemm_ring_kernel<3>", "fc::gemm_decode_kernel<3, 1>",
                 "fc::chain_fused_kernel<4, true>", "fc::chain_fat_kernel<4, true, 48>", "fc::rmsnorm_fused_kernel<4>"):
         assert key in names, key
     assert not any(n.startswith("fc::fce_") or "envelope" in n for n in names)

@@ -86,7 +86,7 @@ def test_big_tile_path_all_plans():
         assert ok, (plan, worst)
 
 
-@pytest.mark.parametrize("M", [1, 16, 17, 256, 4096])
+@pytest.mark.parametrize("M", [1, 16, 17, 64, 256, 4096])
 def test_integer_gemm_exact_in_workspace(M):
     """A, B in {-1,0,1}: plan [1,3] leaves C = A.B (fp16) in the workspace,
     bit-exact against the integer product."""
@@ -174,10 +174,14 @@ def test_gelu_epilogue_accuracy(M, N, K):
         assert np.all(np.abs(Y[0] - ref) <= ulp + 1e-12), (plan, float(np.max(np.abs(Y[0] - ref) / ulp)))
 
 
-# M <= 16 shapes of the split-K decode kernel: no split (one or a few
-# workgroups, or 512 strips), 1-, 2- and 4-step waves, P = 2, 4, 8, 16 and 64.
+# Shapes of the split-K decode kernel.  M <= 16 (one 16-row block): no split
+# (one or a few workgroups, or 512 strips), 1-, 2- and 4-step waves, P = 2, 4,
+# 8, 16 and 64.  17..32 rows (two blocks) and 33..64 rows (four blocks, at most
+# 2 k-steps per wave): no split, P = 2, 8, 16 and 32, ragged row counts.
 DECODE_SHAPES = [(1, 64, 256), (5, 640, 768), (16, 4096, 1024), (16, 4096, 8192), (1, 2048, 2048),
-                 (16, 64, 65536), (7, 16384, 512), (3, 32768, 256)]
+                 (16, 64, 65536), (7, 16384, 512), (3, 32768, 256),
+                 (17, 4096, 4096), (32, 640, 768), (33, 2048, 2048), (64, 4096, 4096), (48, 64, 8192),
+                 (64, 16384, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
@@ -190,15 +194,16 @@ def test_decode_kernel_shapes_all_plans(M, N, K):
         assert ok, (plan, worst)
 
 
+@pytest.mark.parametrize("M", [16, 64])
 @pytest.mark.parametrize("plan", [[4], [1, 3]])
-def test_decode_workspace_reuse(plan):
+def test_decode_workspace_reuse(plan, M):
     """One zero-filled workspace for twelve back-to-back calls on two input
     sets: every result matches the oracle and is bit-identical to the first
     result of its set (the split partials are summed in a fixed order and no
     stale partial from the previous call is read), and the arrival counters
     are zero again afterwards."""
-    M, N, K = 16, 4096, 4096
-    announce(f"gemm decode workspace reuse plan={plan}")
+    N, K = 4096, 4096
+    announce(f"gemm decode workspace reuse plan={plan} M={M}")
     sets = [Dev(M, N, K, salt=21), Dev(M, N, K, salt=22)]
     refs = [oracle.gemm_epilogue_f64(*d.h) for d in sets]
     wsb = fc.fc_gemm_workspace_bytes(M, N, K, plan)
