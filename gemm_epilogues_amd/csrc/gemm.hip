@@ -9,7 +9,7 @@
 //
 // Kernels, by shape: large problems (>= 128 tiles of 256x256, K % 64 == 0) run
 // gemm_ring_kernel (loads straight into a 4-stage LDS ring, B fragments by the
-// transposing LDS read; see its own comment); M <= 64 with N % 64 == 0 and
+// transposing LDS read; see its own comment); M <= 128 with N % 64 == 0 and
 // K % 256 == 0 runs the split-K gemm_decode_kernel; the rest run
 // register-staged kernels (gemm_big_kernel, gemm_epi_kernel) and, for M <= 16
 // without a decode split, gemm_skinny_kernel.
@@ -822,9 +822,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     }
 }
 
-// ------------------------------------------------------------------ decode GEMM (M <= 64, split K)
+// ------------------------------------------------------------------ decode GEMM (M <= 128, split K)
 
-// At M <= 64 the GEMM is a stream over B (K x N fp16), so the layout is
+// At M <= 128 the GEMM is a stream over B (K x N fp16), so the layout is
 // chosen for the stream: every workgroup owns a 64-column strip of B (one
 // full 128-byte line per k-row) and a 1/P share of K, and requests its whole
 // slab (at most 1024 k-rows, 128 KiB) at once with direct-to-LDS loads; its 8
@@ -855,10 +855,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 namespace dec {
 constexpr int WAVES = 8, NT = WAVES * 64, W = 64, ROW = W * 2, KSTEP = 32;
 constexpr int TILE = 16 * W;                                     // outputs per strip and 16-row block
-constexpr int MAXMB = 4;                                         // 16-row blocks: M <= 64
+constexpr int MAXMB = 8;                                         // 16-row blocks: M <= 128
 constexpr int MAXP = 64;
 // k-steps a wave may hold (its A fragments stay in registers): 4 up to 32
-// rows, 2 at 64 rows, keeping the kernel within 128 VGPRs (4 waves per SIMD)
+// rows and 2 beyond, keeping the kernel within 128 VGPRs (4 waves per SIMD)
+// up to 64 rows; at 128 rows it takes up to 256 (2 waves per SIMD)
 __host__ __device__ constexpr int max_steps(int mb) { return mb <= 2 ? 4 : 2; }
 constexpr int MAX_LDS = WAVES * KSTEP * 4 * ROW;                 // 128 KiB
 }
@@ -1036,10 +1037,10 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
     if (threadIdx.x == 0) __hip_atomic_store(counters + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 16-row blocks of the decode kernel for M rows (1, 2 or 4), 0 past 64 rows.
+// 16-row blocks of the decode kernel for M rows (1, 2, 4 or 8), 0 past 128 rows.
 static int decode_blocks(int M)
 {
-    return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 0;
+    return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 16 * dec::MAXMB ? 8 : 0;
 }
 
 // Split of K for the decode kernel: the smallest power of two P with at least
@@ -1147,7 +1148,8 @@ static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bia
         switch (decode_blocks(M)) {
         case 1: return launch_decode<LAST, 1>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
         case 2: return launch_decode<LAST, 2>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
-        default: return launch_decode<LAST, 4>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
+        case 4: return launch_decode<LAST, 4>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
+        default: return launch_decode<LAST, 8>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
         }
     }
     if (M <= 16) {

@@ -92,8 +92,11 @@ def test_decode_workspace_examples():
     assert fc.fc_gemm_workspace_bytes(32, 4096, 4096, [4]) == 256 + 64 * 8 * 2 * 4096
     assert fc.fc_gemm_workspace_bytes(64, 4096, 4096, [4]) == 256 + 64 * 8 * 4 * 4096
     assert fc.fc_gemm_workspace_bytes(40, 2048, 8192, [4]) == 256 + 32 * 16 * 4 * 4096
+    # 65..128 rows: eight blocks, 2 k-steps per wave, one workgroup per CU
+    assert fc.fc_gemm_workspace_bytes(65, 4096, 4096, [4]) == 256 + 64 * 8 * 8 * 4096
+    assert fc.fc_gemm_workspace_bytes(128, 4096, 4096, [4]) == 256 + 64 * 8 * 8 * 4096
     # shapes the decode kernel does not take
-    assert fc.fc_gemm_workspace_bytes(65, 4096, 4096, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(129, 4096, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(16, 4104, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(16, 4096, 4104, [4]) == 0
 

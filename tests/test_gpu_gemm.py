@@ -176,12 +176,13 @@ def test_gelu_epilogue_accuracy(M, N, K):
 
 # Shapes of the split-K decode kernel.  M <= 16 (one 16-row block): no split
 # (one or a few workgroups, or 512 strips), 1-, 2- and 4-step waves, P = 2, 4,
-# 8, 16 and 64.  17..32 rows (two blocks) and 33..64 rows (four blocks, at most
-# 2 k-steps per wave): no split, P = 2, 8, 16 and 32, ragged row counts.
+# 8, 16 and 64.  17..32 rows (two blocks), 33..64 rows (four) and 65..128 rows
+# (eight; at most 2 k-steps per wave beyond 32 rows): no split, P = 2, 4, 8,
+# 16 and 32, ragged row counts.
 DECODE_SHAPES = [(1, 64, 256), (5, 640, 768), (16, 4096, 1024), (16, 4096, 8192), (1, 2048, 2048),
                  (16, 64, 65536), (7, 16384, 512), (3, 32768, 256),
                  (17, 4096, 4096), (32, 640, 768), (33, 2048, 2048), (64, 4096, 4096), (48, 64, 8192),
-                 (64, 16384, 512)]
+                 (64, 16384, 512), (65, 4096, 4096), (100, 640, 1024), (128, 2048, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
@@ -194,7 +195,7 @@ def test_decode_kernel_shapes_all_plans(M, N, K):
         assert ok, (plan, worst)
 
 
-@pytest.mark.parametrize("M", [16, 64])
+@pytest.mark.parametrize("M", [16, 64, 128])
 @pytest.mark.parametrize("plan", [[4], [1, 3]])
 def test_decode_workspace_reuse(plan, M):
     """One zero-filled workspace for twelve back-to-back calls on two input
