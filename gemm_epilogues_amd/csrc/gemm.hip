@@ -7,12 +7,13 @@
 // single fp16 store.  Later segments: pointwise kernels over the fp16 [M,N]
 // intermediate (128-bit loads/stores).
 //
-// Kernels, by shape: large problems (>= 128 tiles of 256x256, K % 64 == 0) run
-// gemm_ring_kernel (loads straight into a 4-stage LDS ring, B fragments by the
-// transposing LDS read; see its own comment); M <= 128 with N % 64 == 0 and
-// K % 256 == 0 runs the split-K gemm_decode_kernel; the rest run
-// register-staged kernels (gemm_big_kernel, gemm_epi_kernel) and, for M <= 16
-// without a decode split, gemm_skinny_kernel.
+// Kernels, by shape: M <= 64 with N % 64 == 0 and K % 256 == 0 runs the
+// split-K gemm_decode_kernel; with K % 64 == 0, large problems (>= 192 tiles of
+// 256x256) run gemm_ring_kernel (loads straight into a 4-stage LDS ring, B
+// fragments by the transposing LDS read; see its own comment) and the rest
+// gemm_ring128_kernel (the same on 128x128 tiles, K split when the tiles are
+// few); other K run register-staged kernels (gemm_big_kernel, gemm_epi_kernel)
+// and, for M <= 16 without a decode split, gemm_skinny_kernel.
 //
 // Register-staged data flow: A [M,K] and B [K,N] are row-major.  Each
 // workgroup owns a BM x BN output tile; K advances in BK slabs through a
@@ -756,6 +757,290 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
     }
 }
 
+// ------------------------------------------------------------------ ring GEMM, 128x128 tiles
+
+// gemm_ring_kernel's dataflow on a quarter of its tile, for problems with too
+// few 256x256 tiles to fill the chip: 4 waves (2 x 2, each 64 x 64 as 2 x 2
+// MFMA tiles), a 4-stage LDS ring of 8 KiB A and 8 KiB B slabs (64 KiB, two
+// workgroups per CU), each wave loading 2 A and 2 B blocks of 1 KiB per slab,
+// fragment addresses computed once (the stage in the offset field).  When
+// even these tiles are too few, K is split over blockIdx.y: each split
+// publishes its fp32 partial tile (64 KiB, in register order, so every access
+// is coalesced and the summing workgroup finds each value in the register it
+// left) with device-scope stores and takes a ticket; the workgroup that draws
+// the last ticket sums the P partials in split order and applies the
+// epilogue.  The partial of a 128x128 tile is a quarter of a 256x256 one, so
+// that last workgroup reads little.
+namespace r128 {
+constexpr int BM = 128, BN = 128, BK = 32, NT = 256, S = 4, WN = 2;
+constexpr int SLAB = BM * BK * 2;            // 8 KiB: one A slab, and one B slab
+constexpr int BREG = S * SLAB;               // the B stages start at 32 KiB
+constexpr int ROWB = BN * 2;                 // bytes per B k-row in LDS
+}
+
+// One k-step's fragments: A [k16][2 tiles], B [k16][2 tiles][2 halves of 4 k].
+struct Ring128Frags {
+    f16x8 a[2][2];
+    u32x2 b[2][2][2];
+};
+// Reads are issued k16-step 0 first (6 of them), then step 1.
+__device__ __forceinline__ void r128_wait0(Ring128Frags &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(6)"
+                 : "+v"(f.a[0][0]), "+v"(f.a[0][1]), "+v"(f.b[0][0][0]), "+v"(f.b[0][0][1]), "+v"(f.b[0][1][0]),
+                   "+v"(f.b[0][1][1]));
+}
+__device__ __forceinline__ void r128_wait1(Ring128Frags &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[1][0]), "+v"(f.a[1][1]), "+v"(f.b[1][0][0]), "+v"(f.b[1][0][1]), "+v"(f.b[1][1][0]),
+                   "+v"(f.b[1][1][1]));
+}
+__device__ __forceinline__ f16x8 r128_bfrag(const Ring128Frags &f, int kk, int j)
+{
+    const u32x4 w = {f.b[kk][j][0].x, f.b[kk][j][0].y, f.b[kk][j][1].x, f.b[kk][j][1].y};
+    return __builtin_bit_cast(f16x8, w);
+}
+
+template <int LAST>
+__global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ bias, const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n, int P, uint32_t *__restrict__ counters,
+    float *__restrict__ partials)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_raw[2 * r128::BREG];
+    __shared__ int is_last;
+    FC_LDS char *lds = (FC_LDS char *)lds_raw;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * r128::BM, n0 = tn * r128::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave / r128::WN, wn = wave % r128::WN;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // split blockIdx.y of P takes k-rows kofs .. kofs + K/P - 1
+    const int split = blockIdx.y, kofs = split * (K / P);
+    const int nk = K / P / r128::BK;             // even
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    // fragment addresses in stage 0 (A: [128 rows][32 k], 16-byte k-units
+    // swizzled by row; B: [32 k][128 n], 32-byte n-units swizzled by k)
+    uint32_t fa[2][2], fb[2][2][2];
+    {
+        const int r = lane & 31, g = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int u = kk * 2 + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wm * 64 + i * 32 + r;
+                fa[kk][i] = lds0 + row * 64 + (u ^ ((row >> 2) & 3)) * 16;
+            }
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const int v = (wn * 64 + jt * 32 + 16 * (g & 1)) >> 4;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = kk * 16 + 8 * (g >> 1) + 4 * hh + (j >> 2);
+                    fb[kk][jt][hh] = lds0 + r128::BREG + k * r128::ROWB + (v ^ (2 * (k & 3))) * 32 + (j & 3) * 8;
+                }
+            }
+        }
+    }
+    // This wave's 2 A blocks (16 rows each) and 2 B blocks (4 k-rows each) of
+    // every slab: lane byte offsets into the workgroup's A panel (rows from
+    // m0, clamped to M-1; the slab adds 2*k0) and into one B slab (k-rows from
+    // k0, columns from n0 clamped to N-8).
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int blk = wave * 2 + q;
+        const int row = blk * 16 + (lane >> 2);
+        const int u = (lane & 3) ^ ((lane >> 4) & 3);      // logical k-unit of this lane's slot
+        const int gm = min(m0 + row, M - 1);
+        la[q] = (uint32_t)((gm - m0) * K + u * 8) * 2u;
+        const int krow = blk * 4 + (lane >> 4);
+        const int p = (lane & 15) >> 1, half = lane & 1;  // physical 32-byte unit, 16-byte half
+        const int v = p ^ (2 * (krow & 3));
+        const int gn = min(n0 + v * 16 + half * 8, N - 8);
+        lb[q] = (uint32_t)(krow * N + (gn - n0)) * 2u;
+    }
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * K), (short)0, 0x7fffffff, ring::RSRC_WORD3);
+    auto issue = [&](int slab, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        const int k0 = kofs + slab * r128::BK;
+        const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(B + (int64_t)k0 * N + n0), (short)0, 0x7fffffff, ring::RSRC_WORD3);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int blk = wave_s * 2 + q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (FC_LDS void *)(lds + ST * r128::SLAB + blk * 1024),
+                                                     16, la[q], k0 * 2, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (FC_LDS void *)(lds + r128::BREG + ST * r128::SLAB + blk * 1024), 16, lb[q], 0, 0, 0);
+        }
+    };
+    issue(0, std::integral_constant<int, 0>{});
+    issue(min(1, nk - 1), std::integral_constant<int, 1>{});
+    issue(min(2, nk - 1), std::integral_constant<int, 2>{});
+    __builtin_amdgcn_s_waitcnt(0xF78);           // vmcnt(8): slab 0 of this wave landed
+    __builtin_amdgcn_s_barrier();                // ... and of every wave
+    Ring128Frags F[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) F[0].a[kk][i] = ring_read_b128<0>(fa[kk][i]);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) F[0].b[kk][jt][hh] = ring_read_tr16<0>(fb[kk][jt][hh]);
+    }
+    // k-step tt; H = tt % 4, so the stage read now is H, the one read next
+    // H+1 and the one loaded now H+3 (mod 4)
+    auto step = [&](int tt, auto hc) __attribute__((always_inline)) {
+        constexpr int H = decltype(hc)::value, cb = H & 1, nb = cb ^ 1;
+        constexpr int SNEXT = ((H + 1) & 3) * r128::SLAB, SLOAD = (H + 3) & 3;
+        r128_wait0(F[cb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(r128_bfrag(F[cb], 0, j), F[cb].a[0][i],
+                                                                   acc[i][j], 0, 0, 0);
+        // slab tt+3 goes to the stage read for step tt-1, which every wave
+        // finished reading before the barrier of step tt-1; past the end a
+        // clamped re-read lands in a stage that is never read
+        issue(min(tt + r128::S - 1, nk - 1), std::integral_constant<int, SLOAD>{});
+        __builtin_amdgcn_s_waitcnt(0xF78);       // vmcnt(8): slab tt+1 of this wave landed
+        r128_wait1(F[cb]);                       // every fragment read of stage tt done
+        __builtin_amdgcn_s_barrier();            // ... in every wave, and slab tt+1 landed
+        __builtin_amdgcn_sched_barrier(0);
+        // the second k16-step's 4 MFMAs, each followed by 3 of the next
+        // step's 12 fragment reads (its k16-step 0 first)
+        ring_static_for<0, 4>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value, i = q >> 1, j = q & 1;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(r128_bfrag(F[cb], 1, j), F[cb].a[1][i], acc[i][j],
+                                                               0, 0, 0);
+            ring_static_for<0, 3>([&](auto rc) __attribute__((always_inline)) {
+                constexpr int rr = 3 * q + decltype(rc)::value, kk = rr / 6, x = rr % 6;
+                if constexpr (x < 2)
+                    F[nb].a[kk][x] = ring_read_b128<SNEXT>(fa[kk][x]);
+                else
+                    F[nb].b[kk][(x - 2) >> 1][(x - 2) & 1] =
+                        ring_read_tr16<SNEXT>(fb[kk][(x - 2) >> 1][(x - 2) & 1]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    int t = 0;
+    for (; t + 4 <= nk; t += 4) {
+        step(t + 0, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+        step(t + 2, std::integral_constant<int, 2>{});
+        step(t + 3, std::integral_constant<int, 3>{});
+    }
+    if (t < nk) {                                // nk % 4 == 2
+        step(t + 0, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);           // drain the clamped prefetches
+    r128_wait0(F[0]);
+    r128_wait1(F[0]);
+    r128_wait0(F[1]);
+    r128_wait1(F[1]);
+
+    if (P > 1) {
+        const int tile = tm * tiles_n + tn;
+        uint64_t *mine = reinterpret_cast<uint64_t *>(partials) + ((int64_t)tile * P + split) * 16 * 256 * 2 +
+                         2 * threadIdx.x;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const f32x16 &a = acc[v >> 3][(v >> 2) & 1];
+            const int q = v & 3;
+            __hip_atomic_store(mine + v * 512, __builtin_bit_cast(uint64_t, make_float2(a[4 * q], a[4 * q + 1])),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + v * 512 + 1,
+                               __builtin_bit_cast(uint64_t, make_float2(a[4 * q + 2], a[4 * q + 3])),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0xF70);       // vmcnt(0): the partial is at the coherence point
+        __syncthreads();
+        if (threadIdx.x == 0)
+            is_last = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      (uint32_t)(P - 1);
+        __syncthreads();
+        if (!is_last) return;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        const uint64_t *base = reinterpret_cast<const uint64_t *>(partials) + (int64_t)tile * P * 16 * 256 * 2 +
+                               2 * threadIdx.x;
+        for (int p = 0; p < P; ++p) {
+            const uint64_t *src = base + (int64_t)p * 16 * 256 * 2;
+#pragma unroll
+            for (int v0 = 0; v0 < 16; v0 += 8) {
+                uint64_t w[8][2];
+#pragma unroll
+                for (int dv = 0; dv < 8; ++dv) {
+                    w[dv][0] = __hip_atomic_load(src + (v0 + dv) * 512, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    w[dv][1] =
+                        __hip_atomic_load(src + (v0 + dv) * 512 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int dv = 0; dv < 8; ++dv) {
+                    const int v = v0 + dv, q = v & 3;
+                    f32x16 &a = acc[v >> 3][(v >> 2) & 1];
+                    const float2 lo = __builtin_bit_cast(float2, w[dv][0]), hi = __builtin_bit_cast(float2, w[dv][1]);
+                    a[4 * q] += lo.x;
+                    a[4 * q + 1] += lo.y;
+                    a[4 * q + 2] += hi.x;
+                    a[4 * q + 3] += hi.y;
+                }
+            }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // Epilogue on the accumulators (C^T layout: lane owns row m = lane % 32 of
+    // tile row i and columns 8g + 4*(lane/32) .. +3 of tile column j).
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm * 64 + i * 32 + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (n >= N) continue;
+                const int64_t o = (int64_t)m * N + n;
+                u32x2 bw = {0u, 0u}, rw = {0u, 0u};
+                if (LAST >= OP_BIAS) bw = *reinterpret_cast<const u32x2 *>(bias + n);
+                if (LAST >= OP_RES) rw = *reinterpret_cast<const u32x2 *>(R + o);
+                u32x2 y;
+                y.x = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 0], f16_lo(bw.x), f16_lo(rw.x)),
+                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 1], f16_hi(bw.x), f16_hi(rw.x)));
+                y.y = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 2], f16_lo(bw.y), f16_lo(rw.y)),
+                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 3], f16_hi(bw.y), f16_hi(rw.y)));
+                *reinterpret_cast<u32x2 *>(out + o) = y;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ skinny GEMM (M <= 16)
 
 // Decode shape: one workgroup per 16-column strip of the output; its waves
@@ -822,9 +1107,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     }
 }
 
-// ------------------------------------------------------------------ decode GEMM (M <= 128, split K)
+// ------------------------------------------------------------------ decode GEMM (M <= 64, split K)
 
-// At M <= 128 the GEMM is a stream over B (K x N fp16), so the layout is
+// At M <= 64 the GEMM is a stream over B (K x N fp16), so the layout is
 // chosen for the stream: every workgroup owns a 64-column strip of B (one
 // full 128-byte line per k-row) and a 1/P share of K, and requests its whole
 // slab (at most 1024 k-rows, 128 KiB) at once with direct-to-LDS loads; its 8
@@ -855,11 +1140,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 namespace dec {
 constexpr int WAVES = 8, NT = WAVES * 64, W = 64, ROW = W * 2, KSTEP = 32;
 constexpr int TILE = 16 * W;                                     // outputs per strip and 16-row block
-constexpr int MAXMB = 8;                                         // 16-row blocks: M <= 128
+constexpr int MAXMB = 4;                                         // 16-row blocks: M <= 64
 constexpr int MAXP = 64;
 // k-steps a wave may hold (its A fragments stay in registers): 4 up to 32
-// rows and 2 beyond, keeping the kernel within 128 VGPRs (4 waves per SIMD)
-// up to 64 rows; at 128 rows it takes up to 256 (2 waves per SIMD)
+// rows, 2 at 64 rows, keeping the kernel within 128 VGPRs (4 waves per SIMD)
 __host__ __device__ constexpr int max_steps(int mb) { return mb <= 2 ? 4 : 2; }
 constexpr int MAX_LDS = WAVES * KSTEP * 4 * ROW;                 // 128 KiB
 }
@@ -1037,10 +1321,12 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
     if (threadIdx.x == 0) __hip_atomic_store(counters + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 16-row blocks of the decode kernel for M rows (1, 2, 4 or 8), 0 past 128 rows.
+// 16-row blocks of the decode kernel for M rows (1, 2 or 4), 0 past 64 rows
+// (from 65 rows the 128x128 ring kernel is faster: 30-34 vs 34-38 us for
+// 65..128 x 4096 x 4096 with eight blocks of 16 rows).
 static int decode_blocks(int M)
 {
-    return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 16 * dec::MAXMB ? 8 : 0;
+    return M <= 16 ? 1 : M <= 32 ? 2 : M <= 16 * dec::MAXMB ? 4 : 0;
 }
 
 // Split of K for the decode kernel: the smallest power of two P with at least
@@ -1063,14 +1349,73 @@ static int decode_splits(int M, int N, int K)
     return best;
 }
 
-// Workspace bytes the decode kernel needs: arrival counters (256-byte
-// rounded) followed by fp32 partials; 0 when P <= 1.
-static size_t decode_scratch_bytes(int M, int N, int K)
+// Split of K for the 128x128 ring kernel: 1 when there are at least 128
+// tiles; else the smallest power of two P up to 16 that brings the grid to
+// 128 workgroups, with every split at least 256 k-rows (8 slabs) deep, else
+// the largest such P (1 when none).  Measured on 129..1024 x 4096 x 4096 and
+// 1024^3, 2048^3: splitting further (to 256 or 512 workgroups) costs more in
+// partial traffic and summing than the extra workgroups gain.
+static int ring128_splits(int M, int N, int K)
 {
-    const int P = decode_splits(M, N, K);
-    if (P <= 1) return 0;
-    const size_t strips = (size_t)(N / dec::W);
-    return ((strips * 4 + 255) & ~(size_t)255) + strips * (size_t)P * decode_blocks(M) * dec::TILE * 4;
+    const int64_t tiles = (int64_t)((M + r128::BM - 1) / r128::BM) * ((N + r128::BN - 1) / r128::BN);
+    int best = 1;
+    if (tiles >= 128) return best;
+    for (int P = 2; P <= 16; P *= 2) {
+        if (K % (64 * P) != 0 || K / P < 256) break;
+        best = P;
+        if (tiles * P >= 128) break;
+    }
+    return best;
+}
+
+// Which kernel runs the GEMM segment of (M, N, K), and its split of K.
+enum GemmRoute { ROUTE_DECODE, ROUTE_SKINNY, ROUTE_RING, ROUTE_RING128, ROUTE_BIG, ROUTE_MID };
+
+static GemmRoute gemm_route(int M, int N, int K, int &P)
+{
+    P = decode_splits(M, N, K);
+    if (P > 0) return ROUTE_DECODE;
+    P = 1;
+    if (M <= 16) return ROUTE_SKINNY;
+    const bool ring_ok = K % 64 == 0 && K <= ring::MAX_K && N <= ring::MAX_N;
+    // the 256x256 ring kernel from 192 tiles (three quarters of the CUs busy);
+    // below that the 128x128 one, two workgroups per CU, is faster (measured
+    // at 2048 x 4096 x 4096, 128 tiles: 101 vs 109 us; at 3072 rows, 192
+    // tiles: 135 vs 119 us the other way)
+    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    if (ring_ok && big_tiles >= 192) return ROUTE_RING;
+    if (ring_ok) {
+        P = ring128_splits(M, N, K);
+        return ROUTE_RING128;
+    }
+    return big_tiles >= 128 ? ROUTE_BIG : ROUTE_MID;
+}
+
+// Split-K scratch inside the caller's workspace, for the decode kernel or the
+// split 128x128 ring kernel: arrival counters (one per strip or tile, 256-byte
+// rounded), then the fp32 partials; both 0 when the shape takes no split.
+static void split_scratch(int M, int N, int K, size_t &counter_bytes, size_t &partial_bytes)
+{
+    counter_bytes = partial_bytes = 0;
+    int P;
+    const GemmRoute route = gemm_route(M, N, K, P);
+    if (P <= 1) return;
+    if (route == ROUTE_DECODE) {
+        const size_t strips = (size_t)(N / dec::W);
+        counter_bytes = (strips * 4 + 255) & ~(size_t)255;
+        partial_bytes = strips * (size_t)P * decode_blocks(M) * dec::TILE * 4;
+    } else if (route == ROUTE_RING128) {
+        const size_t tiles = (size_t)((M + r128::BM - 1) / r128::BM) * ((N + r128::BN - 1) / r128::BN);
+        counter_bytes = (tiles * 4 + 255) & ~(size_t)255;
+        partial_bytes = tiles * (size_t)P * r128::BM * r128::BN * 4;
+    }
+}
+
+static size_t split_scratch_bytes(int M, int N, int K)
+{
+    size_t c, p;
+    split_scratch(M, N, K, c, p);
+    return c + p;
 }
 
 // ------------------------------------------------------------------ pointwise segments
@@ -1117,7 +1462,7 @@ static int launch_gemm_cfg(const uint16_t *A, const uint16_t *B, const uint16_t 
     return launch_status();
 }
 
-// Scratch for the decode kernel inside the caller's workspace.
+// Split-K scratch (decode or 128x128 ring kernel) inside the caller's workspace.
 struct DecodeScratch {
     uint32_t *counters;
     float *partials;
@@ -1141,31 +1486,36 @@ template <int LAST>
 static int launch_gemm(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
                        uint16_t *out, int M, int N, int K, DecodeScratch ds, hipStream_t s)
 {
-    const int P = decode_splits(M, N, K);
-    if (P > 0) {
+    int P;
+    const GemmRoute route = gemm_route(M, N, K, P);
+    if (route == ROUTE_DECODE) {
         const int grid = (N / dec::W) * P;
         const int lds = (K / P) * dec::ROW;
         switch (decode_blocks(M)) {
         case 1: return launch_decode<LAST, 1>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
         case 2: return launch_decode<LAST, 2>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
-        case 4: return launch_decode<LAST, 4>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
-        default: return launch_decode<LAST, 8>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
+        default: return launch_decode<LAST, 4>(A, B, bias, R, out, M, N, K, P, grid, lds, ds, s);
         }
     }
-    if (M <= 16) {
+    if (route == ROUTE_SKINNY) {
         gemm_skinny_kernel<kSkinnyWaves, LAST><<<(N + 15) / 16, kSkinnyWaves * 64, 0, s>>>(
             A, B, bias, R, out, M, N, K);
         return launch_status();
     }
-    // large problems: 256x256 tiles; smaller ones: 128x128 (more workgroups)
-    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (big_tiles >= 128) {
+    if (route == ROUTE_RING) {
+        const int tiles_m = (M + ring::BM - 1) / ring::BM, tiles_n = (N + ring::BN - 1) / ring::BN;
+        gemm_ring_kernel<LAST><<<tiles_m * tiles_n, ring::NT, 0, s>>>(A, B, bias, R, out, M, N, K, tiles_m,
+                                                                     tiles_n);
+        return launch_status();
+    }
+    if (route == ROUTE_RING128) {
+        const int tiles_m = (M + r128::BM - 1) / r128::BM, tiles_n = (N + r128::BN - 1) / r128::BN;
+        gemm_ring128_kernel<LAST><<<dim3(tiles_m * tiles_n, P), r128::NT, 0, s>>>(
+            A, B, bias, R, out, M, N, K, tiles_m, tiles_n, P, ds.counters, ds.partials);
+        return launch_status();
+    }
+    if (route == ROUTE_BIG) {
         const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
-        if (K % 64 == 0 && K <= ring::MAX_K && N <= ring::MAX_N) {
-            gemm_ring_kernel<LAST><<<tiles_m * tiles_n, ring::NT, 0, s>>>(A, B, bias, R, out, M, N, K,
-                                                                         tiles_m, tiles_n);
-            return launch_status();
-        }
         const bool interior = M % big::BM == 0 && N % big::BN == 0 && K % big::BK == 0;
         if (interior)
             gemm_big_kernel<LAST, false><<<tiles_m * tiles_n, big::NT, 0, s>>>(A, B, bias, R, out, M, N, K,
@@ -1233,9 +1583,9 @@ static bool plan_valid(const int *plan, int plan_len)
 
 using namespace fc;
 
-// Workspace layout: [decode counters + partials, when the shape takes the
-// split-K decode kernel][fp16 intermediate, 2MN bytes rounded up to 256, when
-// the plan has a cut].  The counters sit at offset 0 for every plan of a
+// Workspace layout: [split-K counters + partials, when the shape takes the
+// split decode or 128x128 ring kernel][fp16 intermediate, 2MN bytes rounded up
+// to 256, when the plan has a cut].  The counters sit at offset 0 for every plan of a
 // shape, so one workspace serves all plans of that shape.
 static size_t inter_bytes(int M, int N, int plan_len)
 {
@@ -1245,7 +1595,7 @@ static size_t inter_bytes(int M, int N, int plan_len)
 extern "C" size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_len)
 {
     if (!plan_valid(plan, plan_len) || M < 1 || N < 1 || K < 1) return 0;
-    return inter_bytes(M, N, plan_len) + decode_scratch_bytes(M, N, K);
+    return inter_bytes(M, N, plan_len) + split_scratch_bytes(M, N, K);
 }
 
 extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
@@ -1264,7 +1614,9 @@ extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint
         overlaps(Y, mn, bias, (size_t)N * 2) || overlaps(Y, mn, R, mn))
         return FC_ERR_ALIAS;
     const size_t need = fc_gemm_workspace_bytes(M, N, K, plan, plan_len);
-    const size_t dsb = decode_scratch_bytes(M, N, K);
+    size_t counter_bytes, partial_bytes;
+    split_scratch(M, N, K, counter_bytes, partial_bytes);
+    const size_t dsb = counter_bytes + partial_bytes;
     uint16_t *ws = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + dsb);
     DecodeScratch ds = {nullptr, nullptr};
     if (need) {
@@ -1276,9 +1628,8 @@ extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint
             return FC_ERR_ALIAS;
         if (dsb) {
             char *base = static_cast<char *>(workspace);
-            const size_t strips = (size_t)(N / dec::W);
             ds.counters = reinterpret_cast<uint32_t *>(base);
-            ds.partials = reinterpret_cast<float *>(base + ((strips * 4 + 255) & ~(size_t)255));
+            ds.partials = reinterpret_cast<float *>(base + counter_bytes);
         }
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

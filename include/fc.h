@@ -101,9 +101,10 @@ size_t fc_chain_scratch_floats(int64_t n, int K, int mode, int fat_temps);
  *        (round to nearest even).
  *  workspace  device, >= fc_gemm_workspace_bytes() bytes, 16-byte aligned
  *        (NULL allowed when that is 0), not overlapping any operand.  Layout:
- *        first, for shapes with M <= 128 that take the split-K decode kernel,
- *        per-strip arrival counters and fp32 partial sums (D bytes, where
- *        D = fc_gemm_workspace_bytes(M, N, K, {4}, 1)); then, when the plan
+ *        first, for shapes that take a split-K kernel (see
+ *        fc_gemm_workspace_bytes), arrival counters and fp32 partial sums (D
+ *        bytes, where D = fc_gemm_workspace_bytes(M, N, K, {4}, 1)); then, when
+ *        the plan
  *        has a cut, the fp16 intermediate (round_up(2*M*N, 256) bytes at byte
  *        offset D): after a plan whose first segment is the bare GEMM it holds
  *        C = A.B until the next segment overwrites it in place.  The counters
@@ -126,14 +127,19 @@ int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
                      fc_stream stream);
 
 /* Bytes of workspace for (M, N, K, plan): D + round_up(2*M*N, 256) when the
- * plan has a cut, else D, where D is nonzero only when M <= 128, N % 64 == 0
- * and K splits into P > 1 parts for the decode kernel: then, with
- * MB = 1, 2, 4 or 8 blocks of 16 rows (M <= 16, <= 32, <= 64, <= 128),
- * D = round_up(4*N/64, 256) + 64*N*P*MB (counters, then an MB x 16 x 64
- * fp32 partial per 64-column strip and part).  P is the smallest power of two
- * up to 64 with 256*P dividing K, K <= 256*S*P (S = 4 k-steps per wave for
- * MB <= 2, 2 beyond) and (N/64)*P >= 512, else the largest power of two
- * meeting the first two conditions (none: no decode kernel).
+ * plan has a cut, else D, the split-K scratch of the GEMM kernel the shape
+ * takes (0 when it takes no split):
+ *  - M <= 64, N % 64 == 0, K % 256 == 0: the decode kernel, MB = 1, 2 or 4
+ *    blocks of 16 rows (M <= 16, <= 32, <= 64) and K split into P parts, P
+ *    the smallest power of two up to 64 with 256*P dividing K,
+ *    K <= 256*S*P (S = 4 k-steps per wave for MB <= 2, 2 for MB = 4) and
+ *    (N/64)*P >= 512, else the largest one meeting the first two conditions;
+ *    D = round_up(4*N/64, 256) + 64*N*P*MB when P > 1;
+ *  - otherwise, K % 64 == 0 and fewer than 192 tiles of 256x256: the 128x128
+ *    ring kernel over T = ceil(M/128)*ceil(N/128) tiles, K split P ways when
+ *    T < 128 (P the smallest power of two up to 16 with T*P >= 128, 64*P
+ *    dividing K and K/P >= 256, else the largest one meeting the last two);
+ *    D = round_up(4*T, 256) + 65536*T*P when P > 1.
  * 0 for an invalid plan or shape (fc_gemm_epilogue then returns an error). */
 size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_len);
 

@@ -92,13 +92,30 @@ def test_decode_workspace_examples():
     assert fc.fc_gemm_workspace_bytes(32, 4096, 4096, [4]) == 256 + 64 * 8 * 2 * 4096
     assert fc.fc_gemm_workspace_bytes(64, 4096, 4096, [4]) == 256 + 64 * 8 * 4 * 4096
     assert fc.fc_gemm_workspace_bytes(40, 2048, 8192, [4]) == 256 + 32 * 16 * 4 * 4096
-    # 65..128 rows: eight blocks, 2 k-steps per wave, one workgroup per CU
-    assert fc.fc_gemm_workspace_bytes(65, 4096, 4096, [4]) == 256 + 64 * 8 * 8 * 4096
-    assert fc.fc_gemm_workspace_bytes(128, 4096, 4096, [4]) == 256 + 64 * 8 * 8 * 4096
-    # shapes the decode kernel does not take
-    assert fc.fc_gemm_workspace_bytes(129, 4096, 4096, [4]) == 0
+    # shapes the decode kernel does not take: from 65 rows the 128x128 ring
+    # kernel (32 tiles, K split 4 ways)
+    assert fc.fc_gemm_workspace_bytes(65, 4096, 4096, [4]) == 256 + 32 * 4 * 128 * 128 * 4
     assert fc.fc_gemm_workspace_bytes(16, 4104, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(16, 4096, 4104, [4]) == 0
+
+
+def test_ring128_split_workspace_examples():
+    tile = 128 * 128 * 4                       # one fp32 partial tile
+    # 129 rows: 2 x 32 tiles of 128x128, K split 2 ways -> 128 workgroups
+    assert fc.fc_gemm_workspace_bytes(129, 4096, 4096, [4]) == 256 + 64 * 2 * tile
+    assert fc.fc_gemm_workspace_bytes(129, 4096, 4096, [2, 2]) == 256 + 64 * 2 * tile + 2 * 129 * 4096
+    # 200 x 2048: 32 tiles, 4 ways; 1024^3: 64 tiles, 2 ways
+    assert fc.fc_gemm_workspace_bytes(200, 2048, 2048, [4]) == 256 + 32 * 4 * tile
+    assert fc.fc_gemm_workspace_bytes(1024, 1024, 1024, [4]) == 256 + 64 * 2 * tile
+    # 300 x 1000 x 1024: 24 tiles; a split must stay >= 256 deep, so P = 4
+    assert fc.fc_gemm_workspace_bytes(300, 1000, 1024, [4]) == 256 + 24 * 4 * tile
+    # >= 128 tiles of 128x128, >= 192 of 256x256 (the large ring kernel): no split
+    assert fc.fc_gemm_workspace_bytes(512, 4096, 4096, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(2048, 4096, 4096, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(4096, 4096, 4096, [4]) == 0
+    # too shallow to split (K / 2 < 256), or K % 64 != 0 (register-staged kernels)
+    assert fc.fc_gemm_workspace_bytes(129, 4096, 256, [4]) == 0
+    assert fc.fc_gemm_workspace_bytes(129, 4096, 4000, [4]) == 0
 
 
 @pytest.mark.parametrize("plan", [[], [0, 4], [5], [1, 1, 1], [2, -1, 3], [1, 1, 1, 1, 0]])

@@ -176,13 +176,12 @@ def test_gelu_epilogue_accuracy(M, N, K):
 
 # Shapes of the split-K decode kernel.  M <= 16 (one 16-row block): no split
 # (one or a few workgroups, or 512 strips), 1-, 2- and 4-step waves, P = 2, 4,
-# 8, 16 and 64.  17..32 rows (two blocks), 33..64 rows (four) and 65..128 rows
-# (eight; at most 2 k-steps per wave beyond 32 rows): no split, P = 2, 4, 8,
-# 16 and 32, ragged row counts.
+# 8, 16 and 64.  17..32 rows (two blocks) and 33..64 rows (four blocks, at
+# most 2 k-steps per wave): no split, P = 2, 8, 16 and 32, ragged row counts.
 DECODE_SHAPES = [(1, 64, 256), (5, 640, 768), (16, 4096, 1024), (16, 4096, 8192), (1, 2048, 2048),
                  (16, 64, 65536), (7, 16384, 512), (3, 32768, 256),
                  (17, 4096, 4096), (32, 640, 768), (33, 2048, 2048), (64, 4096, 4096), (48, 64, 8192),
-                 (64, 16384, 512), (65, 4096, 4096), (100, 640, 1024), (128, 2048, 2048)]
+                 (64, 16384, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
@@ -195,7 +194,7 @@ def test_decode_kernel_shapes_all_plans(M, N, K):
         assert ok, (plan, worst)
 
 
-@pytest.mark.parametrize("M", [16, 64, 128])
+@pytest.mark.parametrize("M", [16, 64])
 @pytest.mark.parametrize("plan", [[4], [1, 3]])
 def test_decode_workspace_reuse(plan, M):
     """One zero-filled workspace for twelve back-to-back calls on two input
@@ -243,3 +242,63 @@ def test_decode_workspace_shared_by_plans():
     for plan, Y in Ys:
         ok, worst = tol_ok(bits(Y), ref)
         assert ok, (plan, worst)
+
+
+# Shapes with fewer than 192 tiles of 256x256 and K % 64 == 0 (and beyond the
+# decode kernel) run the 128x128 ring kernel, K split P ways when its tiles
+# number fewer than 128 (the last workgroup of a tile sums the fp32 partials in
+# split order): from 65 rows on, P = 4, 4, 4, 2, 4, 4, 2 and 2, ragged rows
+# and columns included.
+RING128_SHAPES = [(65, 4096, 4096), (100, 640, 1024), (128, 2048, 2048), (129, 4096, 4096), (300, 1000, 1024),
+                  (200, 2048, 2048), (1024, 1024, 1024), (520, 264, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", RING128_SHAPES)
+def test_ring128_shapes_all_plans(M, N, K):
+    announce(f"gemm ring128 M={M} N={N} K={K} all plans")
+    assert fc.fc_gemm_workspace_bytes(M, N, K, [4]) > 0      # the split path is the one under test
+    d = Dev(M, N, K, salt=11 * M + N + K)
+    ref = oracle.gemm_epilogue_f64(*d.h)
+    for plan in ALL_PLANS:
+        ok, worst = tol_ok(d.run(plan), ref)
+        assert ok, (plan, worst)
+
+
+def test_ring128_512_sampled():
+    """512 x 4096 x 4096 (128 tiles of 128x128, no split): sampled outputs,
+    tile corners included, for the named plans."""
+    announce("gemm ring128 512x4096x4096 sampled")
+    M, N, K = 512, 4096, 4096
+    d = Dev(M, N, K, salt=5)
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([rng.integers(0, M, 3000), [0, 511, 127, 128, 511, 0]])
+    cols = np.concatenate([rng.integers(0, N, 3000), [0, 4095, 128, 127, 0, 4095]])
+    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
+    for plan in NAMED_PLANS:
+        ok, worst = tol_ok(d.run(plan)[rows, cols], ref)
+        assert ok, (plan, worst)
+
+
+def test_ring128_workspace_reuse():
+    """One zero-filled workspace for twelve back-to-back calls on two input
+    sets of a split shape: every result matches the oracle and equals the
+    first result of its set bit for bit, and the tile counters end at zero."""
+    M, N, K = 200, 2048, 2048
+    announce("gemm ring128 workspace reuse")
+    sets = [Dev(M, N, K, salt=31), Dev(M, N, K, salt=32)]
+    refs = [oracle.gemm_epilogue_f64(*d.h) for d in sets]
+    ws = torch.zeros(fc.fc_gemm_workspace_bytes(M, N, K, [4]), dtype=torch.uint8, device="cuda")
+    Ys = []
+    for it in range(12):
+        d = sets[it % 2]
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fc.fc_gemm_epilogue(d.A, d.B, d.bias, d.R, Y, [4], ws)
+        Ys.append(Y)
+    torch.cuda.synchronize()
+    outs = [bits(Y) for Y in Ys]
+    for it, y in enumerate(outs):
+        ok, worst = tol_ok(y, refs[it % 2])
+        assert ok, (it, worst)
+        assert np.array_equal(y, outs[it % 2]), it
+    tiles = ((M + 127) // 128) * ((N + 127) // 128)
+    assert not ws[: 4 * tiles].cpu().numpy().view(np.uint32).any()
