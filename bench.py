@@ -130,19 +130,17 @@ def load_traffic(kernel_key, src):
     return row.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole passes of the fused chain (K in {2,3,4,6,8}, n = 16,777,216) and
-    of the causal softmax over [2048, 2048] heads, repeated until about
-    `budget_s` seconds of host work; reported in the same unit (algorithmic
-    GB/s).  The GEMM epilogue is timed on sampled outputs of the 4096^3 chain."""
+def oracle_stream_rate(budget_s, heads_per_pass=16):
+    """Algorithmic GB/s of the oracle on whole passes of the fused chain (K in
+    {2,3,4,6,8}, n = 16,777,216) and of the causal softmax over [2048, 2048]
+    heads, repeated until about `budget_s` seconds of host work.  Returns
+    (GB/s, chain passes, chain seconds, heads, softmax seconds)."""
     import numpy as np
 
     import oracle
     import synth
     from oracle import ledger
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     n = CHAIN_N
     x, _, _ = synth.chain_inputs(n, 1)
     coefs = [synth.chain_inputs(1, K)[1:] for K in CHAIN_KS]
@@ -158,13 +156,59 @@ def cpu_baseline(budget_s=12.0):
         t_chain += time.perf_counter() - t0
         chain_passes += 1
         t0 = time.perf_counter()
-        for _ in range(16):
+        for _ in range(heads_per_pass):
             oracle.causal_softmax_rows(s, SCALE, rows)
         t_sm += time.perf_counter() - t0
-        heads += 16
+        heads += heads_per_pass
     chain_bytes = chain_passes * sum(ledger.chain_bytes(n, K, True) for K in CHAIN_KS)
     sm_bytes = heads * ledger.softmax_bytes(1, S, 64, True)
-    gbps = (chain_bytes + sm_bytes) / (t_chain + t_sm) / 1e9
+    return (chain_bytes + sm_bytes) / (t_chain + t_sm) / 1e9, chain_passes, t_chain, heads, t_sm
+
+
+def _oracle_single_thread(budget_s=4.0):
+    """The same stream sample on one host thread, in a child process (the
+    oracle's OpenMP pool is sized when it starts; the child touches no GPU)."""
+    import subprocess
+    code = ("import json, sys; sys.path.insert(0, %r); import bench; "
+            "r = bench.oracle_stream_rate(%r, heads_per_pass=2); print(json.dumps(r))") % (ROOT, budget_s)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120,
+                             check=True).stdout.strip().splitlines()[-1]
+        gbps, passes, t_c, heads, t_s = json.loads(out)
+    except Exception as e:                      # reported, never fatal to the GPU measurement
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1,
+            "sample": f"{passes} chain pass(es) ({t_c:.1f}s) and {heads} softmax heads ({t_s:.1f}s) on one thread"}
+
+
+def _host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "model": model}
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole passes of the fused chain and of the causal softmax (see
+    oracle_stream_rate) for about `budget_s` seconds on the host's OpenMP
+    threads, and the same sample on one thread; reported in the same unit
+    (algorithmic GB/s).  The GEMM epilogue is timed on sampled outputs of the
+    4096^3 chain, attention on every query row of 8 heads."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    gbps, chain_passes, t_chain, heads, t_sm = oracle_stream_rate(budget_s)
     M, N, K = GEMM_MNK
     A, B, bias, R = synth.gemm_inputs(M, N, K)
     cnt = 262144
@@ -191,6 +235,8 @@ def cpu_baseline(budget_s=12.0):
                           "sample": f"{cnt} sampled outputs of the 4096^3 chain (2*K flops each) in {t_g:.1f}s"},
         "attention": {"value": round(att_tflops, 6), "unit": "TFLOP/s",
                       "sample": f"all query rows of {att_heads} [2048, 128] heads (causal flops) in {t_a:.1f}s"},
+        "single_thread": _oracle_single_thread(),
+        "host": _host_cpu(),
     }
 
 
