@@ -653,20 +653,24 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
     }
     const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(A + (int64_t)m0 * K), (short)0, 0x7fffffff, ring::RSRC_WORD3);
-    // slab `slab` into stage ST
-    auto issue = [&](int slab, auto stage) __attribute__((always_inline)) {
-        constexpr int ST = decltype(stage)::value;
+    // load X of slab `slab` into stage ST (X = 0..3: A block X/2 when X is
+    // even, B block X/2 when odd)
+    auto issue1 = [&](int slab, auto stage, auto xc) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value, X = decltype(xc)::value, q = X >> 1;
         const int k0 = slab * ring::BK;
-        const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(B + (int64_t)k0 * N + n0), (short)0, 0x7fffffff, ring::RSRC_WORD3);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int blk = wave_s * 2 + q;
+        const int blk = wave_s * 2 + q;
+        if constexpr ((X & 1) == 0) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (FC_LDS void *)(lds + ST * ring::SLAB + blk * 1024),
                                                      16, la[q], k0 * 2, 0, 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(B + (int64_t)k0 * N + n0), (short)0, 0x7fffffff, ring::RSRC_WORD3);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc_b, (FC_LDS void *)(lds + ring::BREG + ST * ring::SLAB + blk * 1024), 16, lb[q], 0, 0, 0);
         }
+    };
+    auto issue = [&](int slab, auto stage) __attribute__((always_inline)) {
+        ring_static_for<0, 4>([&](auto xc) __attribute__((always_inline)) { issue1(slab, stage, xc); });
     };
     issue(0, std::integral_constant<int, 0>{});
     issue(min(1, nk - 1), std::integral_constant<int, 1>{});
@@ -690,17 +694,23 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
         constexpr int SNEXT = ((H + 1) & 3) * ring::SLAB, SLOAD = (H + 3) & 3;
         frag_wait0(F[cb]);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 0, j), F[cb].a[0][i],
-                                                                   acc[i][j], 0, 0, 0);
-        // slab tt+3 goes to the stage read for step tt-1: every wave read its
-        // fragments for step tt-1 during step tt-2 and waited for all of them
-        // before the barrier of step tt-1; past the end a clamped re-read
-        // lands in a stage that is never read
-        issue(min(tt + ring::S - 1, nk - 1), std::integral_constant<int, SLOAD>{});
+        // The first k16-step's 8 MFMAs, one of the wave's 4 loads of slab tt+3
+        // after every second: issued in one burst after the MFMAs, the loads of
+        // all waves queue together and stall the MFMA issue (1,127 vs 1,066
+        // cycles per k-step; 0.9 % less time, the clock falls with the denser
+        // MFMA issue).  Slab tt+3 goes to the stage read for step tt-1:
+        // every wave read its fragments for step tt-1 during step tt-2 and
+        // waited for all of them before the barrier of step tt-1; past the end
+        // a clamped re-read lands in a stage that is never read.
+        const int lslab = min(tt + ring::S - 1, nk - 1);
+        ring_static_for<0, 8>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value, i = q >> 1, j = q & 1;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring_bfrag(F[cb], 0, j), F[cb].a[0][i], acc[i][j],
+                                                               0, 0, 0);
+            if constexpr ((q & 1) != 0)
+                issue1(lslab, std::integral_constant<int, SLOAD>{}, std::integral_constant<int, (q >> 1)>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
         __builtin_amdgcn_s_waitcnt(0xF78);       // vmcnt(8): slab tt+1 of this wave landed
         frag_wait1(F[cb]);                       // every fragment read of stage tt done
         __builtin_amdgcn_s_barrier();            // ... in every wave, and slab tt+1 landed
@@ -919,7 +929,9 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
                                                                    acc[i][j], 0, 0, 0);
         // slab tt+3 goes to the stage read for step tt-1, which every wave
         // finished reading before the barrier of step tt-1; past the end a
-        // clamped re-read lands in a stage that is never read
+        // clamped re-read lands in a stage that is never read.  (Spreading the
+        // four loads between these MFMAs, as the 256x256 kernel does, was 2.7 %
+        // slower here: this kernel's LDS port is the busier one.)
         issue(min(tt + r128::S - 1, nk - 1), std::integral_constant<int, SLOAD>{});
         __builtin_amdgcn_s_waitcnt(0xF78);       // vmcnt(8): slab tt+1 of this wave landed
         r128_wait1(F[cb]);                       // every fragment read of stage tt done
