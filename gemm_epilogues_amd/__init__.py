@@ -174,6 +174,22 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _call_workspace(nbytes: int, device, stream, zero: bool):
+    """A workspace the binding owns for one call.  It is allocated (and
+    zero-filled) on the launch stream, so the fill is ordered before the
+    kernels and torch's caching allocator hands the block out again only to
+    later work on that same stream."""
+    torch = _torch()
+    if stream is None:
+        s = torch.cuda.current_stream(device)
+    elif isinstance(stream, int):
+        s = torch.cuda.ExternalStream(stream, device=device)
+    else:
+        s = stream
+    with torch.cuda.stream(s):
+        return (torch.zeros if zero else torch.empty)(nbytes, dtype=torch.uint8, device=device)
+
+
 def _dev(t, dtype, name):
     torch = _torch()
     if t is None:
@@ -235,7 +251,8 @@ def fc_gemm_epilogue(A, B, bias, R, Y, plan: Sequence[int], workspace=None, stre
     """Y = GELU(A@B + bias) + R, fp16 device tensors A [M,K], B [K,N], bias [N], R/Y [M,N].
 
     A caller-supplied workspace must be zero-filled before its first use (see
-    fc_gemm_workspace_bytes); without one, a zero-filled one is allocated."""
+    fc_gemm_workspace_bytes); without one, a zero-filled one is allocated on
+    the launch stream for this call."""
     torch = _torch()
     for t, nm in ((A, "A"), (B, "B"), (bias, "bias"), (R, "R"), (Y, "Y")):
         _dev(t, torch.float16, nm)
@@ -250,8 +267,8 @@ def fc_gemm_epilogue(A, B, bias, R, Y, plan: Sequence[int], workspace=None, stre
     if workspace is None:
         need = int(_lib.fc_gemm_workspace_bytes(M, N, K, arr, n))
         if need:
-            # zero-filled, as the decode kernel's arrival counters require
-            workspace = torch.zeros(need, dtype=torch.uint8, device=A.device)
+            # zero-filled, as the split kernels' arrival counters require
+            workspace = _call_workspace(need, A.device, stream, zero=True)
     if workspace is not None:
         if not workspace.is_cuda:
             raise ValueError("workspace must be a device tensor")
@@ -381,7 +398,7 @@ def fc_rmsnorm(x, g, y, eps: float, mode: int = FC_RMSNORM_FUSED, workspace=None
     if workspace is None and mode == FC_RMSNORM_UNFUSED:
         need = fc_rmsnorm_workspace_bytes(rows, d, mode)
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = _call_workspace(need, x.device, stream, zero=False)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     rc = _lib.fc_rmsnorm(_ptr(x), _ptr(g), _ptr(y), int(rows), int(d), float(eps), int(mode),

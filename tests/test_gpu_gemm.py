@@ -302,3 +302,37 @@ def test_ring128_workspace_reuse():
         assert np.array_equal(y, outs[it % 2]), it
     tiles = ((M + 127) // 128) * ((N + 127) // 128)
     assert not ws[: 4 * tiles].cpu().numpy().view(np.uint32).any()
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (200, 2048, 2048)])
+def test_side_stream_without_workspace(M, N, K):
+    """No workspace passed and a stream other than torch's current one: the
+    binding zero-fills its own workspace on that stream, so the split kernels'
+    arrival counters are zero when they run; every plan matches the oracle and
+    the default-stream result bit for bit, also with a busy current stream."""
+    announce(f"gemm side stream, binding-owned workspace {M}x{N}x{K}")
+    d = Dev(M, N, K, salt=31)
+    ref = oracle.gemm_epilogue_f64(*d.h)
+    side = torch.cuda.Stream()
+    for plan in NAMED_PLANS:
+        base = d.run(plan)
+        outs = []
+        for handle in (side, side.cuda_stream):      # a torch stream, then a raw handle
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            # a freed block of the workspace's size full of 0xFF on the current
+            # stream, then work left queued there: a workspace taken and filled
+            # on the current stream would reach the kernels unfilled
+            need = fc.fc_gemm_workspace_bytes(M, N, K, plan)
+            dirty = torch.full((max(need, 1),), 255, dtype=torch.uint8, device="cuda")
+            del dirty
+            side.wait_stream(torch.cuda.current_stream())
+            busy = torch.empty(1 << 24, device="cuda").normal_()
+            fc.fc_gemm_epilogue(d.A, d.B, d.bias, d.R, Y, plan, None, stream=handle)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            del busy
+            outs.append(bits(Y))
+        for y in outs:
+            ok, worst = tol_ok(y, ref)
+            assert ok, (plan, worst)
+            assert np.array_equal(y, base), plan

@@ -65,3 +65,23 @@ def test_many_short_rows():
         ref = oracle.rmsnorm_f64(x, g, 1e-5)
         y = run(x, g, 1e-5, mode).astype(np.float64)
         assert np.all(np.abs(y - ref) <= 4e-6 * np.abs(ref)), mode
+
+
+def test_unfused_on_a_side_stream_without_workspace():
+    """The four-pass form on a stream other than torch's current one, with
+    the binding allocating its workspace: allocated on that stream, so its
+    passes and the caching allocator's reuse are ordered; matches the
+    default-stream result bit for bit."""
+    announce("rmsnorm unfused, side stream, binding-owned workspace")
+    rows, d = 64, 4096
+    x, g = inputs(rows, d, 77)
+    base = run(x, g, 1e-5, 1)
+    xd, gd = torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda()
+    side = torch.cuda.Stream()
+    for handle in (side, side.cuda_stream):
+        yd = torch.empty_like(xd)
+        side.wait_stream(torch.cuda.current_stream())
+        fc.fc_rmsnorm(xd, gd, yd, 1e-5, 1, None, stream=handle)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert np.array_equal(yd.cpu().numpy(), base)
