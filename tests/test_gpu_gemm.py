@@ -135,15 +135,17 @@ def test_square_4096_config_sampled():
         assert np.max(np.abs(y - ys[(4,)]) / (1 + np.abs(ys[(4,)]))) <= 1e-2, p
 
 
-def test_ring_path_ragged_all_plans():
-    """K % 64 == 0 and >= 128 tiles: the direct-to-LDS ring kernel, with M and N
-    tails (clamped rows/columns are computed but never stored)."""
-    M, N, K = 2085, 4136, 320
+@pytest.mark.parametrize("M,N,K", [(2085, 4136, 320), (3109, 4136, 320), (4096 + 200, 4096 - 8, 192)])
+def test_ring_path_ragged_all_plans(M, N, K):
+    """K % 64 == 0 with M and N tails (clamped rows/columns are computed but
+    never stored): 153 tiles of 256x256 take the 128x128 ring kernel, 221 and
+    272 take the 256x256 one."""
     announce(f"gemm ring path M={M} N={N} K={K}")
     d = Dev(M, N, K, salt=11)
     rng = np.random.default_rng(3)
-    rows = np.concatenate([rng.integers(0, M, 3000), [0, M - 1, 2047, 2048, 255, 256]])
-    cols = np.concatenate([rng.integers(0, N, 3000), [0, N - 1, 4095, 4096, 255, 256]])
+    edges = np.array([0, 255, 256, 2047, 2048, 4095, 4096])
+    rows = np.concatenate([rng.integers(0, M, 3000), np.minimum(edges, M - 1), [M - 1]])
+    cols = np.concatenate([rng.integers(0, N, 3000), np.minimum(edges, N - 1), [N - 1]])
     ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
     for plan in ALL_PLANS:
         Y = d.run(plan)
