@@ -8,8 +8,8 @@
 // intermediate (128-bit loads/stores).
 //
 // Kernels, by shape: M <= 64 with N % 64 == 0 and K % 256 == 0 runs the
-// split-K gemm_decode_kernel; with K % 64 == 0, large problems (>= 192 tiles of
-// 256x256) run gemm_ring_kernel (loads straight into a 4-stage LDS ring, B
+// split-K gemm_decode_kernel; with K % 64 == 0, large problems (more than 512
+// tiles of 128x128) run gemm_ring_kernel (loads straight into a 4-stage LDS ring, B
 // fragments by the transposing LDS read; see its own comment) and the rest
 // gemm_ring128_kernel (the same on 128x128 tiles, K split when the tiles are
 // few); other K run register-staged kernels (gemm_big_kernel, gemm_epi_kernel)
@@ -1390,12 +1390,14 @@ static GemmRoute gemm_route(int M, int N, int K, int &P)
     P = 1;
     if (M <= 16) return ROUTE_SKINNY;
     const bool ring_ok = K % 64 == 0 && K <= ring::MAX_K && N <= ring::MAX_N;
-    // the 256x256 ring kernel from 192 tiles (three quarters of the CUs busy);
-    // below that the 128x128 one, two workgroups per CU, is faster (measured
-    // at 2048 x 4096 x 4096, 128 tiles: 101 vs 109 us; at 3072 rows, 192
-    // tiles: 135 vs 119 us the other way)
+    // The 128x128 ring kernel while its tiles fit in one round of two
+    // workgroups on each of the 256 CUs; past that the 256x256 one, whose
+    // round holds four times the work (measured: 2048 x 4096 x 4096, 512
+    // small tiles: 101 vs 109 us; 2088 x 4072, 544 small tiles and a second
+    // round of 32: 123 vs 98 us; 3072 rows: 135 vs 119 us)
     const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (ring_ok && big_tiles >= 192) return ROUTE_RING;
+    const int64_t small_tiles = (int64_t)((M + r128::BM - 1) / r128::BM) * ((N + r128::BN - 1) / r128::BN);
+    if (ring_ok && small_tiles > 512) return ROUTE_RING;
     if (ring_ok) {
         P = ring128_splits(M, N, K);
         return ROUTE_RING128;

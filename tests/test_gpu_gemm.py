@@ -135,11 +135,12 @@ def test_square_4096_config_sampled():
         assert np.max(np.abs(y - ys[(4,)]) / (1 + np.abs(ys[(4,)]))) <= 1e-2, p
 
 
-@pytest.mark.parametrize("M,N,K", [(2085, 4136, 320), (3109, 4136, 320), (4096 + 200, 4096 - 8, 192)])
+@pytest.mark.parametrize("M,N,K", [(1000, 2000, 320), (2085, 4136, 320), (3109, 4136, 320),
+                                   (4096 + 200, 4096 - 8, 192)])
 def test_ring_path_ragged_all_plans(M, N, K):
     """K % 64 == 0 with M and N tails (clamped rows/columns are computed but
-    never stored): 153 tiles of 256x256 take the 128x128 ring kernel, 221 and
-    272 take the 256x256 one."""
+    never stored): 128 tiles of 128x128 (one round) take the 128x128 ring
+    kernel unsplit; 561, 825 and 1088 take the 256x256 one."""
     announce(f"gemm ring path M={M} N={N} K={K}")
     d = Dev(M, N, K, salt=11)
     rng = np.random.default_rng(3)
