@@ -53,6 +53,15 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
 {
     return (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
 }
+// The same rounding (to nearest even) as pack_f16x2, in one gfx950
+// v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float lo, float hi)
+{
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
 __device__ __forceinline__ float f16_lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
