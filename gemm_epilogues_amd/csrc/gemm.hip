@@ -1063,7 +1063,47 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
     }
 
     // Epilogue on the accumulators (C^T layout: lane owns row m = lane % 32 of
-    // tile row i and columns 8g + 4*(lane/32) .. +3 of tile column j).
+    // tile row i and columns 8g + 4*(lane/32) .. +3 of tile column j), laid
+    // out as the 256x256 kernel's: bias converted once, interior tiles through
+    // one row pointer with constant column offsets.
+    float bf[2][4][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+            u32x2 bw = {0u, 0u};
+            if (LAST >= OP_BIAS && n < N) bw = *reinterpret_cast<const u32x2 *>(bias + n);
+            bf[j][g][0] = f16_lo(bw.x);
+            bf[j][g][1] = f16_hi(bw.x);
+            bf[j][g][2] = f16_lo(bw.y);
+            bf[j][g][3] = f16_hi(bw.y);
+        }
+    auto out4 = [&](int i, int j, int g, u32x2 rw) __attribute__((always_inline)) {
+        u32x2 y;
+        y.x = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 0], bf[j][g][0], f16_lo(rw.x)),
+                             apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 1], bf[j][g][1], f16_hi(rw.x)));
+        y.y = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 2], bf[j][g][2], f16_lo(rw.y)),
+                             apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 3], bf[j][g][3], f16_hi(rw.y)));
+        return y;
+    };
+    if (m0 + r128::BM <= M && n0 + r128::BN <= N) {
+        const int64_t base = (int64_t)(m0 + wm * 64 + (lane & 31)) * N + n0 + wn * 64 + 4 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint16_t *Rr = R + base + (int64_t)i * 32 * N;
+            uint16_t *Yr = out + base + (int64_t)i * 32 * N;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 rw = {0u, 0u};
+                    if (LAST >= OP_RES) rw = *reinterpret_cast<const u32x2 *>(Rr + j * 32 + 8 * g);
+                    *reinterpret_cast<u32x2 *>(Yr + j * 32 + 8 * g) = out4(i, j, g, rw);
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int m = m0 + wm * 64 + i * 32 + (lane & 31);
@@ -1075,15 +1115,9 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
                 const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
                 if (n >= N) continue;
                 const int64_t o = (int64_t)m * N + n;
-                u32x2 bw = {0u, 0u}, rw = {0u, 0u};
-                if (LAST >= OP_BIAS) bw = *reinterpret_cast<const u32x2 *>(bias + n);
+                u32x2 rw = {0u, 0u};
                 if (LAST >= OP_RES) rw = *reinterpret_cast<const u32x2 *>(R + o);
-                u32x2 y;
-                y.x = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 0], f16_lo(bw.x), f16_lo(rw.x)),
-                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 1], f16_hi(bw.x), f16_hi(rw.x)));
-                y.y = pack_f16x2(apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 2], f16_lo(bw.y), f16_lo(rw.y)),
-                                 apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 3], f16_hi(bw.y), f16_hi(rw.y)));
-                *reinterpret_cast<u32x2 *>(out + o) = y;
+                *reinterpret_cast<u32x2 *>(out + o) = out4(i, j, g, rw);
             }
         }
     }
