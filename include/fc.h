@@ -135,8 +135,8 @@ int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
  *    K <= 256*S*P (S = 4 k-steps per wave for MB <= 2, 2 for MB = 4) and
  *    (N/64)*P >= 512, else the largest one meeting the first two conditions;
  *    D = round_up(4*N/64, 256) + 64*N*P*MB when P > 1;
- *  - otherwise, K % 64 == 0 and fewer than 192 tiles of 256x256: the 128x128
- *    ring kernel over T = ceil(M/128)*ceil(N/128) tiles, K split P ways when
+ *  - otherwise, K % 64 == 0 and T = ceil(M/128)*ceil(N/128) <= 512: the
+ *    128x128 ring kernel over those T tiles, K split P ways when
  *    T < 128 (P the smallest power of two up to 16 with T*P >= 128, 64*P
  *    dividing K and K/P >= 256, else the largest one meeting the last two);
  *    D = round_up(4*T, 256) + 65536*T*P when P > 1.

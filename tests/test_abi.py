@@ -109,7 +109,7 @@ def test_ring128_split_workspace_examples():
     assert fc.fc_gemm_workspace_bytes(1024, 1024, 1024, [4]) == 256 + 64 * 2 * tile
     # 300 x 1000 x 1024: 24 tiles; a split must stay >= 256 deep, so P = 4
     assert fc.fc_gemm_workspace_bytes(300, 1000, 1024, [4]) == 256 + 24 * 4 * tile
-    # >= 128 tiles of 128x128, >= 192 of 256x256 (the large ring kernel): no split
+    # 128..512 tiles of 128x128, or more than 512 (the 256x256 ring kernel): no split
     assert fc.fc_gemm_workspace_bytes(512, 4096, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(2048, 4096, 4096, [4]) == 0
     assert fc.fc_gemm_workspace_bytes(4096, 4096, 4096, [4]) == 0

@@ -247,7 +247,7 @@ def test_decode_workspace_shared_by_plans():
         assert ok, (plan, worst)
 
 
-# Shapes with fewer than 192 tiles of 256x256 and K % 64 == 0 (and beyond the
+# Shapes with at most 512 tiles of 128x128 and K % 64 == 0 (and beyond the
 # decode kernel) run the 128x128 ring kernel, K split P ways when its tiles
 # number fewer than 128 (the last workgroup of a tile sums the fp32 partials in
 # split order): from 65 rows on, P = 4, 4, 4, 2, 4, 4, 2 and 2, ragged rows
