@@ -103,8 +103,6 @@ static int dispatch_fat(const float *x, float *y, int64_t n, const ChainCoef &c,
     return FC_OK;
 }
 
-static bool fat_stages_ok(int K) { return K == 1 || K == 2 || K == 3 || K == 4 || K == 6 || K == 8; }
-
 bool chain_fat_supported(int K, int temps)
 {
     const bool k_ok = K == 1 || K == 2 || K == 3 || K == 4 || K == 6 || K == 8;

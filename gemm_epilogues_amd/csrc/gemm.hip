@@ -26,6 +26,15 @@
 
 #include <type_traits>
 
+// The split-K handoffs of gemm_ring128_kernel and gemm_decode_kernel publish
+// fp32 partials and count arrivals without release/acquire fences (those
+// write back and invalidate a whole XCD's L2 per workgroup).  They rely on
+// the memory model of the gfx9 family as gfx950 implements it; see the
+// comment at the first handoff.  Another target needs that argument redone.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "gemm.hip is written for gfx950: its split-K handoff relies on that ISA's memory model"
+#endif
+
 namespace fc {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -1021,6 +1030,22 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
                                __builtin_bit_cast(uint64_t, make_float2(a[4 * q + 2], a[4 * q + 3])),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        // Handoff without fences.  What it relies on (gfx9 family, gfx950):
+        //  1. an agent-scope atomic store is a global store with the device
+        //     scope bit set: it writes through this XCD's L2 to the device
+        //     coherence point, and its completion is acknowledged from there;
+        //  2. on gfx9 the vector memory counter also counts stores (there is no
+        //     separate store counter), so s_waitcnt vmcnt(0) returns only once
+        //     every partial store of this thread is complete at that point;
+        //  3. the barrier after the wait orders every thread's completed stores
+        //     before thread 0's ticket, an agent-scope atomic performed at the
+        //     same coherence point;
+        //  4. the last workgroup reads partials with agent-scope atomic loads,
+        //     which bypass its own XCD's L2 and read the coherence point, so
+        //     they cannot hit a stale line.
+        // A compiler that moved a store past the wait, or a target without (1)
+        // or (2), would break this silently; the guard at the top of the file
+        // keeps other targets out.
         __builtin_amdgcn_s_waitcnt(0xF70);       // vmcnt(0): the partial is at the coherence point
         __syncthreads();
         if (threadIdx.x == 0)
@@ -1369,6 +1394,9 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
         __hip_atomic_store(reinterpret_cast<uint64_t *>(partials + pbase + rb * dec::TILE),
                            __builtin_bit_cast(uint64_t, make_float2(v0[rb], v1[rb])), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    // the same fence-free handoff as gemm_ring128_kernel's (the four rules
+    // listed there): device-scope stores, vmcnt(0), barrier, ticket, and
+    // device-scope loads by the last workgroup
     __builtin_amdgcn_s_waitcnt(0xF70);                            // vmcnt(0): the partial is at the coherence point
     __syncthreads();
     if (threadIdx.x == 0)

@@ -187,8 +187,11 @@ static int launch_fused(const uint16_t *s, OutT *out, int64_t rows, int S, float
 // else element by element.
 #define FC_ROW_VEC(S) (((S) & 7) == 0)
 
-// (1) row max of scale*s over the whole row (the mask is not applied here;
-// any shift gives the same softmax).
+// (1) row max of scale*s over the keys the row keeps (j <= i, from the
+// indices).  The whole row is read, as the step's byte count has it; taking
+// the max over kept keys only keeps every exp(x) of a kept key <= 1 whatever
+// the masked scores hold (a masked score far above the kept ones would
+// otherwise underflow every kept exponential).
 __global__ __launch_bounds__(kSmBlock) void um_rowmax_kernel(const uint16_t *__restrict__ s,
                                                              float *__restrict__ rmax, int64_t rows,
                                                              int S, float scale)
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(kSmBlock) void um_rowmax_kernel(const uint16_t *__r
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
+    const int i = (int)(row % S);
     const uint16_t *p = s + row * (int64_t)S;
     float m = -INFINITY;
     if (FC_ROW_VEC(S)) {
@@ -203,10 +207,12 @@ __global__ __launch_bounds__(kSmBlock) void um_rowmax_kernel(const uint16_t *__r
             float f[8];
             unpack8(*reinterpret_cast<const u32x4 *>(p + j0), f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, f[e] * scale);
+            for (int e = 0; e < 8; ++e)
+                if (j0 + e <= i) m = fmaxf(m, f[e] * scale);
         }
     } else {
-        for (int j = lane; j < S; j += 64) m = fmaxf(m, bf16_lo(p[j]) * scale);
+        for (int j = lane; j < S; j += 64)
+            if (j <= i) m = fmaxf(m, bf16_lo(p[j]) * scale);
     }
     m = wave_max(m);
     if (lane == 0) rmax[row] = m;
@@ -237,7 +243,9 @@ __global__ __launch_bounds__(kSmBlock) void um_sub_kernel(const uint16_t *__rest
     }
 }
 
-// (3) e = exp(x) * mask  (in place in out)
+// (3) e = exp(x) where the mask is 1, else 0 (in place in out).  The mask
+// selects rather than multiplies: x of a masked key may be large, and
+// exp(x) * 0 would be NaN once exp(x) overflows.
 __global__ __launch_bounds__(kSmBlock) void um_expmask_kernel(uint16_t *__restrict__ out,
                                                               const uint16_t *__restrict__ mask,
                                                               int64_t rows, int S)
@@ -253,12 +261,12 @@ __global__ __launch_bounds__(kSmBlock) void um_expmask_kernel(uint16_t *__restri
             unpack8(*reinterpret_cast<const u32x4 *>(q + j0), f);
             unpack8(*reinterpret_cast<const u32x4 *>(mk + j0), g);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = fast_exp2(f[e] * kLog2e) * g[e];
+            for (int e = 0; e < 8; ++e) f[e] = g[e] != 0.0f ? fast_exp2(f[e] * kLog2e) : 0.0f;
             store8(q + j0, f);
         }
     } else {
         for (int j = lane; j < S; j += 64)
-            store1(q + j, fast_exp2(bf16_lo(q[j]) * kLog2e) * bf16_lo(mk[j]));
+            store1(q + j, bf16_lo(mk[j]) != 0.0f ? fast_exp2(bf16_lo(q[j]) * kLog2e) : 0.0f);
     }
 }
 

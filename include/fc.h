@@ -77,7 +77,17 @@ enum { FC_RMSNORM_FUSED = 0, FC_RMSNORM_UNFUSED = 1 };
 int fc_chain(const float *x, float *y, int64_t n, const float *a, const float *b, int K,
              int relu_even, int mode, float *scratch, int fat_temps, fc_stream stream);
 
-/* Floats of scratch fc_chain needs for (n, K, mode, fat_temps); 0 if none. */
+/* Floats of scratch fc_chain needs for (n, K, mode, fat_temps); 0 if none.
+ * NAIVE with K >= 2: n (the second ping-pong buffer of "C-05", section 3, API
+ * table, naive row).  FAT: 4 * L, one fp32x4 sink entry per lane of the
+ * launch, L = 256 * min(2048, max(1, ceil(floor(n/4) / 256))); lane l visits
+ * the fp32x4 vectors q = l, l + L, l + 2L, ... of x (the n mod 4 trailing
+ * elements are computed without temporaries and do not enter the sink) and
+ * writes sink[4l .. 4l+3] = per component, the sum over its vectors of
+ * t_0 + (t_1 + (... + t_{T-1})), where t_j = fmaf(0.5, t_{j-1}, y_{s(j)}),
+ * t_{-1} = 0, y_s the element's chain value after stage s and its ReLU and
+ * s(j) = floor(j*K/T) (the fat row of the same table gives no formula; this
+ * one keeps all T temporaries live).  FUSED: 0. */
 size_t fc_chain_scratch_floats(int64_t n, int K, int mode, int fat_temps);
 
 /* -------------------------------------------------------- GEMM + epilogue */
@@ -126,7 +136,9 @@ int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
                      const int *plan, int plan_len, void *workspace, size_t ws_bytes,
                      fc_stream stream);
 
-/* Bytes of workspace for (M, N, K, plan): D + round_up(2*M*N, 256) when the
+/* Bytes of workspace for (M, N, K, plan) ("K4 讲解", section 1: every cut of
+ * a plan writes one [M,N] fp16 intermediate that the next kernel reads back;
+ * the split-K scratch is this library's own): D + round_up(2*M*N, 256) when the
  * plan has a cut, else D, the split-K scratch of the GEMM kernel the shape
  * takes (0 when it takes no split):
  *  - M <= 64, N % 64 == 0, K % 256 == 0: the decode kernel, MB = 1, 2 or 4
@@ -161,9 +173,11 @@ size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_le
  *          of the row is written as zeros without being read.  UNFUSED: ignored.
  *  mode    FC_SOFTMAX_FUSED: one kernel, one pass over the kept tiles.
  *          FC_SOFTMAX_UNFUSED: the five-step baseline -- row max of scale*s over
- *          the whole row; x = scale*s - max; e = exp(x) * mask; row sum; e/sum
- *          -- each step its own kernel, bf16 intermediates in `out`, fp32 row
- *          statistics, and a materialised bf16 0/1 mask.
+ *          the kept keys (the whole row is read); x = scale*s - max; e = exp(x)
+ *          where the mask is 1, else 0; row sum; e/sum -- each step its own
+ *          kernel, bf16 intermediates in `out`, fp32 row statistics, and a
+ *          materialised bf16 0/1 mask.  Masked scores never reach the result,
+ *          whatever they hold (inf and NaN included).
  *  workspace  UNFUSED: device, >= fc_softmax_workspace_bytes() bytes, laid out
  *          as [mask bf16 BH*S*S, padded to a multiple of 256 bytes]
  *          [row max fp32 BH*S][row sum fp32 BH*S]; the
@@ -183,11 +197,18 @@ int fc_causal_softmax_f32out(const uint16_t *scores, float *out, int64_t BH, int
 int fc_causal_softmax_tiles(const uint16_t *scores, uint16_t *out, int32_t *tiles_per_row,
                             int64_t BH, int S, float scale, int tile, fc_stream stream);
 
-/* Writes the causal mask as bf16 1.0 (key j <= query i) / 0.0 (j > i) into
- * mask [BH, S, S] (device, 16-byte aligned). */
+/* The unfused baseline's materialised mask ("AIGC 基本功", appendix byte
+ * ledger, attention-tail entry: five score-sized steps plus one materialised
+ * mask of the score tensor's size): writes bf16 1.0 where key j <= query i
+ * and 0.0 where j > i into mask [BH, S, S] (device, 16-byte aligned; the
+ * first part of the UNFUSED workspace).  BH >= 1, S >= 1; FC_ERR_NULL /
+ * FC_ERR_SHAPE / FC_ERR_ALIGN before any launch, FC_ERR_HIP if it fails. */
 int fc_causal_mask_materialise(uint16_t *mask, int64_t BH, int S, fc_stream stream);
 
-/* UNFUSED: round_up(2*BH*S*S, 256) + 8*BH*S bytes; FUSED: 0. */
+/* Workspace of fc_causal_softmax: UNFUSED round_up(2*BH*S*S, 256) + 8*BH*S
+ * bytes (the materialised mask of the appendix ledger's attention-tail entry,
+ * then the fp32 row max and row sum the five steps pass between kernels);
+ * FUSED 0.  0 for invalid arguments. */
 size_t fc_softmax_workspace_bytes(int64_t BH, int S, int mode);
 
 /* ------------------------------------------------------------ causal attention */

@@ -54,6 +54,9 @@ def _load():
         sig = {
             "oracle_chain_f64": [P, P, I64, P, P, I, I],
             "oracle_chain_f32fma": [P, P, I64, P, P, I, I],
+            "oracle_chain_fat_sink_f64": [P, I64, P, P, I, I, I, I64, P, P],
+            "oracle_chain_fat_sink_f32": [P, I64, P, P, I, I, I, I64, P],
+            "oracle_epilogue_on_product_f64": [P, P, P, I64, I64, P],
             "oracle_gemm_f64": [P, P, I64, I64, I64, P],
             "oracle_gemm_epilogue_f64": [P, P, P, P, I64, I64, I64, P],
             "oracle_gemm_epilogue_at": [P, P, P, P, I64, I64, I64, P, P, I64, P],
@@ -104,6 +107,30 @@ def chain_f32fma(x, a, b, relu_even: bool = True) -> np.ndarray:
     return y
 
 
+def chain_fat_sink_f64(x, a, b, relu_even: bool, temps: int, lanes: int, with_abs: bool = False):
+    """Sink of the fat probe ("C-05" section 3, fat row) in fp64: 4*lanes values,
+    sink[4*lane + c] = sum over the lane's vectors q = lane, lane+lanes, ... of
+    sum_j t_j, t_j = t_{j-1}/2 + y_{floor(jK/T)}.  With ``with_abs`` also the
+    same sums of |t_j| (the error scale of an fp32 evaluation)."""
+    x, a, b = _c(x, np.float32), _c(a, np.float32), _c(b, np.float32)
+    assert a.shape == b.shape and lanes >= 1 and temps >= 0
+    sink = np.empty(4 * lanes, dtype=np.float64)
+    absd = np.empty(4 * lanes, dtype=np.float64) if with_abs else None
+    _load().oracle_chain_fat_sink_f64(_p(x), x.size, _p(a), _p(b), a.size, int(relu_even), int(temps),
+                                      int(lanes), _p(sink), _p(absd) if with_abs else None)
+    return (sink, absd) if with_abs else sink
+
+
+def chain_fat_sink_f32(x, a, b, relu_even: bool, temps: int, lanes: int) -> np.ndarray:
+    """The same sink with every step one fp32 rounding, in the probe's order."""
+    x, a, b = _c(x, np.float32), _c(a, np.float32), _c(b, np.float32)
+    assert a.shape == b.shape and lanes >= 1 and temps >= 0
+    sink = np.empty(4 * lanes, dtype=np.float32)
+    _load().oracle_chain_fat_sink_f32(_p(x), x.size, _p(a), _p(b), a.size, int(relu_even), int(temps),
+                                      int(lanes), _p(sink))
+    return sink
+
+
 # ---------------------------------------------------------------- gemm + epilogue
 
 def gelu(z: float) -> float:
@@ -137,6 +164,21 @@ def gemm_epilogue_f64(A, B, bias, R) -> np.ndarray:
     assert B.shape[0] == K and bias.shape == (N,) and R.shape == (M, N)
     Y = np.empty((M, N), dtype=np.float64)
     _load().oracle_gemm_epilogue_f64(_p(A), _p(B), _p(bias), _p(R), M, N, K, _p(Y))
+    return Y
+
+
+def gemm_epilogue_f64_matmul(A, B, bias, R) -> np.ndarray:
+    """The same Y with the product step taken by numpy's fp64 matrix product
+    (a library primitive; fp16 -> fp64 is exact) and the bias, GELU and
+    residual stages by the C oracle: fast enough for 4096^3 in a test."""
+    A, B, bias, R = (_c(t, np.uint16) for t in (A, B, bias, R))
+    M, K = A.shape
+    N = B.shape[1]
+    assert B.shape[0] == K and bias.shape == (N,) and R.shape == (M, N)
+    C = np.ascontiguousarray(np.matmul(A.view(np.float16).astype(np.float64),
+                                       B.view(np.float16).astype(np.float64)))
+    Y = np.empty((M, N), dtype=np.float64)
+    _load().oracle_epilogue_on_product_f64(_p(C), _p(bias), _p(R), M, N, _p(Y))
     return Y
 
 

@@ -97,6 +97,109 @@ void oracle_chain_f32fma(const float *x, float *y, int64_t n,
     }
 }
 
+/* ------------------------------------------------------------ fat-probe sink */
+
+/*
+ * The fat row of "C-05", section 3 (API table): the fused chain plus T live
+ * temporaries per thread, added into a sink so that none can be dropped.  The
+ * pages give the idea, not a formula; the formula read here is:
+ *  - elements go in vectors of four, v = x[4q .. 4q+3], q = 0 .. n/4 - 1; the
+ *    n mod 4 trailing elements are not part of any vector and never reach the
+ *    sink;
+ *  - vector q belongs to lane q mod L of the L lanes of the launch, and a lane
+ *    visits its vectors in increasing q;
+ *  - for one element with chain values y_s (after stage s and its ReLU):
+ *      t_{-1} = 0,  t_j = t_{j-1} / 2 + y_{s(j)},  s(j) = floor(j K / T),
+ *      j = 0 .. T-1, and the element's term is t_0 + t_1 + ... + t_{T-1};
+ *  - sink[4 lane + c] = sum of the terms of component c over the lane's vectors.
+ * T = 0 leaves the sink zero.  L, the lane count, is the launch's.
+ */
+static void fat_lane_f64(const float *x, int64_t nvec, const float *a, const float *b, int K,
+                         int relu_even, int T, int64_t lanes, int64_t lane, double *sink,
+                         double *abs_sink)
+{
+    for (int c = 0; c < 4; ++c) {
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t q = lane; q < nvec; q += lanes) {
+            double y = (double)x[4 * q + c];
+            double t = 0.0, term = 0.0, term_abs = 0.0;
+            int j = 0;
+            for (int s = 0; s < K; ++s) {
+                y = (double)a[s] * y + (double)b[s];
+                if (relu_even && (s % 2) == 0 && y < 0.0)
+                    y = 0.0;
+                for (; j < T && ((int64_t)j * K) / T == s; ++j) {
+                    t = 0.5 * t + y;
+                    term += t;
+                    term_abs += fabs(t);
+                }
+            }
+            acc += term;
+            acc_abs += term_abs;
+        }
+        sink[4 * lane + c] = acc;
+        if (abs_sink)
+            abs_sink[4 * lane + c] = acc_abs;
+    }
+}
+
+/* fp64 sink (and, if abs_sink is not NULL, the same sums of |t_j|, the scale
+ * of the rounding error of any fp32 evaluation).  sink: 4 * lanes doubles. */
+void oracle_chain_fat_sink_f64(const float *x, int64_t n, const float *a, const float *b, int K,
+                               int relu_even, int T, int64_t lanes, double *sink,
+                               double *abs_sink)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t lane = 0; lane < lanes; ++lane)
+        fat_lane_f64(x, n / 4, a, b, K, relu_even, T, lanes, lane, sink, abs_sink);
+}
+
+/*
+ * The same sink evaluated the way a single-precision thread evaluates it: one
+ * correctly rounded fmaf per chain stage, t_j = fmaf(0.5, t_{j-1}, y_{s(j)}),
+ * the element's terms added from the last one back,
+ * t_0 + (t_1 + (... + (t_{T-2} + t_{T-1}))), and the lane's running fp32 sum
+ * taking one term per vector in visiting order.  Every operation is a single
+ * IEEE rounding, so this predicts the bits of any evaluation in that order.
+ */
+void oracle_chain_fat_sink_f32(const float *x, int64_t n, const float *a, const float *b, int K,
+                               int relu_even, int T, int64_t lanes, float *sink)
+{
+    const int64_t nvec = n / 4;
+    #pragma omp parallel
+    {
+        float *t = (float *)malloc((size_t)(T > 0 ? T : 1) * sizeof(float));
+        #pragma omp for schedule(static)
+        for (int64_t lane = 0; lane < lanes; ++lane) {
+            for (int c = 0; c < 4; ++c) {
+                float acc = 0.0f;
+                for (int64_t q = lane; q < nvec && t; q += lanes) {
+                    float y = x[4 * q + c];
+                    float prev = 0.0f;
+                    int j = 0;
+                    for (int s = 0; s < K; ++s) {
+                        y = fmaf(a[s], y, b[s]);
+                        if (relu_even && (s % 2) == 0 && y < 0.0f)
+                            y = 0.0f;
+                        for (; j < T && ((int64_t)j * K) / T == s; ++j) {
+                            prev = fmaf(0.5f, prev, y);
+                            t[j] = prev;
+                        }
+                    }
+                    if (T > 0) {
+                        float r = t[T - 1];
+                        for (int jj = T - 2; jj >= 0; --jj)
+                            r = t[jj] + r;
+                        acc = acc + r;
+                    }
+                }
+                sink[4 * lane + c] = t ? acc : NAN;
+            }
+        }
+        free(t);
+    }
+}
+
 /* ------------------------------------------------------------ GEMM + epilogue */
 
 /* GELU in its erf form: z * Phi(z) = 0.5 * z * (1 + erf(z / sqrt(2))). */
@@ -128,14 +231,19 @@ void oracle_gemm_f64(const uint16_t *A, const uint16_t *B,
  * The four-stage chain of "K4 讲解", section 1, on one output element:
  *   C = A.B ; C' = C + bias[j] ; C'' = GELU(C') ; Y = C'' + R[i,j].
  */
+static double epilogue_of(double c, const uint16_t *bias, const uint16_t *R,
+                          int64_t N, int64_t i, int64_t j)
+{
+    double c1 = c + half_bits_to_double(bias[j]);
+    double c2 = oracle_gelu(c1);
+    return c2 + half_bits_to_double(R[i * N + j]);
+}
+
 static double epilogue_at(const uint16_t *A, const uint16_t *B,
                           const uint16_t *bias, const uint16_t *R,
                           int64_t N, int64_t K, int64_t i, int64_t j)
 {
-    double c = dot_f16(A, B, N, K, i, j);
-    double c1 = c + half_bits_to_double(bias[j]);
-    double c2 = oracle_gelu(c1);
-    return c2 + half_bits_to_double(R[i * N + j]);
+    return epilogue_of(dot_f16(A, B, N, K, i, j), bias, R, N, i, j);
 }
 
 void oracle_gemm_epilogue_f64(const uint16_t *A, const uint16_t *B,
@@ -146,6 +254,17 @@ void oracle_gemm_epilogue_f64(const uint16_t *A, const uint16_t *B,
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j)
             Y[i * N + j] = epilogue_at(A, B, bias, R, N, K, i, j);
+}
+
+/* The chain's last three stages on a product C = A.B (fp64 [M,N]) that the
+ * caller formed with a library matrix product: Y = GELU(C + bias) + R. */
+void oracle_epilogue_on_product_f64(const double *C, const uint16_t *bias, const uint16_t *R,
+                                    int64_t M, int64_t N, double *Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            Y[i * N + j] = epilogue_of(C[i * N + j], bias, R, N, i, j);
 }
 
 /* Same chain at cnt sampled (row, col) positions. */

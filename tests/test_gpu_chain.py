@@ -114,16 +114,67 @@ def test_relu_chain_config_full_size(K):
             assert (y >= 0).all()          # last stage is even -> ReLU
 
 
+def lanes_of(n, K, temps):
+    """Lanes of the fat launch: the sink holds one fp32x4 per lane."""
+    return fc.fc_chain_scratch_floats(n, K, fc.FC_CHAIN_FAT, temps) // 4
+
+
+def check_fat(x, a, b, relu, temps, xd=None):
+    """Fat y equals the oracle's one-rounding chain bit for bit (and the fp64
+    chain normwise within 1e-6); the sink equals the oracle's fp32 evaluation
+    of its formula exactly and the fp64 one within 64 u of the sum of
+    |t_j| (T + K + the lane's vector count roundings, each at most u of it)."""
+    n, K = x.size, a.size
+    xd = f32(x) if xd is None else xd
+    y, sink = run(xd, a, b, relu, fc.FC_CHAIN_FAT, fat_temps=temps)
+    ref32 = oracle.chain_f32fma(x, a, b, relu)
+    assert np.array_equal(y, ref32), np.flatnonzero(y != ref32)[:5]
+    assert normwise(y, oracle.chain_f64(x, a, b, relu)) <= 1e-6
+    lanes = lanes_of(n, K, temps)
+    assert sink.size == 4 * lanes
+    s32 = oracle.chain_fat_sink_f32(x, a, b, relu, temps, lanes)
+    # values, not bits: a ReLU may leave -0.0 or +0.0 (either is accepted)
+    bad = np.flatnonzero(~(sink == s32))
+    assert bad.size == 0, (bad[:5], sink[bad[:5]], s32[bad[:5]])
+    s64, absd = oracle.chain_fat_sink_f64(x, a, b, relu, temps, lanes, with_abs=True)
+    assert np.all(np.abs(sink.astype(np.float64) - s64) <= 64 * 2.0 ** -24 * absd + 1e-30)
+    if temps:
+        assert np.abs(sink).sum() > 0
+
+
 @pytest.mark.parametrize("temps", [0, 16, 48, 96, 128])
-def test_fat_probe_equals_fused(temps):
-    """K = 4 fat probe: y bit-identical to fused; the sink is finite."""
-    announce(f"fat K=4 temps={temps}")
+def test_fat_probe_small_with_tail(temps):
+    """K = 4 fat probe on 2^20 + 5 elements (a ragged tail the sink skips):
+    y and the sink against the oracle, y bit-identical to the fused kernel."""
+    announce(f"fat K=4 temps={temps} n=2^20+5")
     n = (1 << 20) + 5
     x, a, b = synth.chain_inputs(n, 4, salt=77)
     xd = f32(x)
+    check_fat(x, a, b, True, temps, xd)
     yf, _ = run(xd, a, b, True, fc.FC_CHAIN_FUSED)
-    yt, sink = run(xd, a, b, True, fc.FC_CHAIN_FAT, fat_temps=temps)
+    yt, _ = run(xd, a, b, True, fc.FC_CHAIN_FAT, fat_temps=temps)
     assert np.array_equal(yf.view(np.uint32), yt.view(np.uint32))
-    assert np.isfinite(sink).all()
-    if temps:
-        assert np.abs(sink).sum() > 0
+
+
+@pytest.fixture(scope="module")
+def full_chain_inputs():
+    cache = {}
+
+    def get(K):
+        if K not in cache:
+            announce(f"generating chain inputs n=16777216 K={K}")
+            x, a, b = synth.chain_inputs(16777216, K)
+            cache.clear()
+            cache[K] = (x, a, b, f32(x))
+        return cache[K]
+    return get
+
+
+@pytest.mark.parametrize("K,temps", [(4, 0), (4, 16), (4, 48), (4, 96), (4, 128),
+                                     (2, 48), (3, 48), (6, 48), (8, 48)])
+def test_fat_probe_full_size(full_chain_inputs, K, temps):
+    """n = 16,777,216 (the chain workload): the fat probe at the T sweep's
+    points (K = 4) and at T = 48 for every K, y and sink against the oracle."""
+    announce(f"fat full size n=16777216 K={K} temps={temps}")
+    x, a, b, xd = full_chain_inputs(K)
+    check_fat(x, a, b, True, temps, xd)

@@ -57,6 +57,21 @@ class Dev:
         return bits(Y)
 
 
+def check_every_output(d, plans):
+    """Every output of every plan against the full fp64 reference (product by
+    numpy's fp64 matmul, epilogue by the C oracle), compared on the device."""
+    ref = torch.from_numpy(oracle.gemm_epilogue_f64_matmul(*d.h)).cuda()
+    bound = 1e-2 * (1.0 + ref.abs())
+    for plan in plans:
+        Y = torch.empty((d.M, d.N), dtype=torch.float16, device="cuda")
+        wsb = fc.fc_gemm_workspace_bytes(d.M, d.N, d.K, plan)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+        fc.fc_gemm_epilogue(d.A, d.B, d.bias, d.R, Y, plan, ws)
+        torch.cuda.synchronize()
+        worst = float(((Y.double() - ref).abs() / bound).max())
+        assert worst <= 1.0, (plan, worst)
+
+
 SMALL = [(1, 8, 8), (3, 16, 40), (16, 64, 64), (17, 40, 24), (33, 72, 136), (64, 128, 256),
          (100, 264, 520), (129, 136, 72), (256, 256, 64), (300, 520, 1000)]
 
@@ -72,18 +87,11 @@ def test_all_plans_small_shapes(M, N, K):
 
 
 def test_big_tile_path_all_plans():
-    """Shapes that take the 256x256 tile kernel (>= 128 tiles), with ragged M."""
+    """Shapes that take the 256x256 tile kernel (>= 128 tiles), with ragged M:
+    every output of every plan."""
     M, N, K = 2048 + 37, 4096, 264
     announce(f"gemm big tiles M={M} N={N} K={K}")
-    d = Dev(M, N, K, salt=5)
-    rng = np.random.default_rng(1)
-    rows = np.concatenate([rng.integers(0, M, 3000), [0, M - 1, 255, 256, 2047, 2048]])
-    cols = np.concatenate([rng.integers(0, N, 3000), [0, N - 1, 255, 256, 31, 32]])
-    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
-    for plan in ALL_PLANS:
-        Y = d.run(plan)
-        ok, worst = tol_ok(Y[rows, cols], ref)
-        assert ok, (plan, worst)
+    check_every_output(Dev(M, N, K, salt=5), ALL_PLANS)
 
 
 @pytest.mark.parametrize("M", [1, 16, 17, 64, 256, 4096])
@@ -116,23 +124,35 @@ def test_decode_config_all_plans():
     assert np.max(np.abs(y4 - ref) / (1 + np.abs(ref))) <= 2.0 ** -10
 
 
-def test_square_4096_config_sampled():
-    """M = N = K = 4096: sampled outputs (incl. tile corners) against the oracle."""
-    announce("gemm 4096^3 sampled")
+@pytest.fixture(scope="module")
+def square_4096():
+    """The 4096^3 workload and its full fp64 reference, computed once (the
+    product step by numpy's fp64 matmul, the epilogue by the C oracle)."""
+    announce("gemm 4096^3: generating inputs and the full fp64 reference")
     d = Dev(4096, 4096, 4096)
-    rng = np.random.default_rng(2)
-    rows = np.concatenate([rng.integers(0, 4096, 4000), [0, 4095, 255, 256, 4095, 0]])
-    cols = np.concatenate([rng.integers(0, 4096, 4000), [0, 4095, 256, 255, 0, 4095]])
-    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
-    ys = {}
-    for plan in NAMED_PLANS:
-        Y = d.run(plan)
-        ok, worst = tol_ok(Y[rows, cols], ref)
-        assert ok, (plan, worst)
-        ys[tuple(plan)] = Y.view(np.float16).astype(np.float32)
-    # plans differ only by fp16 rounding at the cuts
-    for p, y in ys.items():
-        assert np.max(np.abs(y - ys[(4,)]) / (1 + np.abs(ys[(4,)]))) <= 1e-2, p
+    ref = torch.from_numpy(oracle.gemm_epilogue_f64_matmul(*d.h)).cuda()
+    return d, ref
+
+
+def test_square_4096_config_every_output(square_4096):
+    """M = N = K = 4096, all eight split plans: every output within
+    1e-2 (1 + |ref|) of the fp64 oracle (compared on the device in fp64), and
+    the fused plan, whose only rounding is the final one, within 2^-10."""
+    d, ref = square_4096
+    bound = 1e-2 * (1.0 + ref.abs())
+    for plan in ALL_PLANS:
+        announce(f"gemm 4096^3 plan={plan} every output")
+        Y = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
+        wsb = fc.fc_gemm_workspace_bytes(4096, 4096, 4096, plan)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+        fc.fc_gemm_epilogue(d.A, d.B, d.bias, d.R, Y, plan, ws)
+        torch.cuda.synchronize()
+        err = (Y.double() - ref).abs()
+        worst = float((err / bound).max())
+        assert worst <= 1.0, (plan, worst)
+        if plan == [4]:
+            assert float((err / (1.0 + ref.abs())).max()) <= 2.0 ** -10
+        del Y, ws, err
 
 
 @pytest.mark.parametrize("M,N,K", [(1000, 2000, 320), (2085, 4136, 320), (3109, 4136, 320),
@@ -140,18 +160,9 @@ def test_square_4096_config_sampled():
 def test_ring_path_ragged_all_plans(M, N, K):
     """K % 64 == 0 with M and N tails (clamped rows/columns are computed but
     never stored): 128 tiles of 128x128 (one round) take the 128x128 ring
-    kernel unsplit; 561, 825 and 1088 take the 256x256 one."""
+    kernel unsplit; 561, 825 and 1088 take the 256x256 one.  Every output."""
     announce(f"gemm ring path M={M} N={N} K={K}")
-    d = Dev(M, N, K, salt=11)
-    rng = np.random.default_rng(3)
-    edges = np.array([0, 255, 256, 2047, 2048, 4095, 4096])
-    rows = np.concatenate([rng.integers(0, M, 3000), np.minimum(edges, M - 1), [M - 1]])
-    cols = np.concatenate([rng.integers(0, N, 3000), np.minimum(edges, N - 1), [N - 1]])
-    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
-    for plan in ALL_PLANS:
-        Y = d.run(plan)
-        ok, worst = tol_ok(Y[rows, cols], ref)
-        assert ok, (plan, worst)
+    check_every_output(Dev(M, N, K, salt=11), ALL_PLANS)
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 4096, 64), (300, 520, 64), (4096, 4096, 64)])
@@ -267,19 +278,11 @@ def test_ring128_shapes_all_plans(M, N, K):
         assert ok, (plan, worst)
 
 
-def test_ring128_512_sampled():
-    """512 x 4096 x 4096 (128 tiles of 128x128, no split): sampled outputs,
-    tile corners included, for the named plans."""
-    announce("gemm ring128 512x4096x4096 sampled")
-    M, N, K = 512, 4096, 4096
-    d = Dev(M, N, K, salt=5)
-    rng = np.random.default_rng(3)
-    rows = np.concatenate([rng.integers(0, M, 3000), [0, 511, 127, 128, 511, 0]])
-    cols = np.concatenate([rng.integers(0, N, 3000), [0, 4095, 128, 127, 0, 4095]])
-    ref = oracle.gemm_epilogue_at(*d.h, rows, cols)
-    for plan in NAMED_PLANS:
-        ok, worst = tol_ok(d.run(plan)[rows, cols], ref)
-        assert ok, (plan, worst)
+def test_ring128_512_every_output():
+    """512 x 4096 x 4096 (128 tiles of 128x128, no split): every output of
+    every plan."""
+    announce("gemm ring128 512x4096x4096 every output")
+    check_every_output(Dev(512, 4096, 4096, salt=5), ALL_PLANS)
 
 
 def test_ring128_workspace_reuse():

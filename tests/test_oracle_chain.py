@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from exact import exact_chain, f32_value
+from exact import exact_chain, f32_rne, f32_value
 from conftest import load_golden
 
 
@@ -105,3 +105,127 @@ def test_fp32_chain_error_level_matches_pages():
     page = {r["n"]: r["rel_err"] for r in g["rows"]}[n]
     assert 1e-8 <= err <= 2 * page, (err, page)
     assert normwise(oracle.chain_f64(x, a, b, relu_even=False), ref) <= 1e-13
+
+
+# ---------------------------------------------------------------- fat-probe sink
+# The sink of the fat row ("C-05", section 3, API table) as read here: vector q
+# of four elements belongs to lane q mod L; per element t_j = t_{j-1}/2 +
+# y_{floor(jK/T)} (y_s the chain value after stage s), the element's term is
+# sum_j t_j, and a lane adds its vectors' terms per component.
+
+
+def _fat_sink_exact(x, a, b, relu, T, lanes, round_each=False):
+    """Exact rational sink written from the definition (independent of the C
+    code): optionally every step rounded to fp32, in the probe's order."""
+    K = len(a)
+    nvec = len(x) // 4
+    out = [Fraction(0)] * (4 * lanes)
+    rnd = f32_rne if round_each else (lambda v: v)
+    for lane in range(lanes):
+        for c in range(4):
+            acc = Fraction(0)
+            for q in range(lane, nvec, lanes):
+                ys = []
+                y = f32_value(x[4 * q + c])
+                for s in range(K):
+                    y = rnd(f32_value(a[s]) * y + f32_value(b[s]))
+                    if relu and s % 2 == 0 and y < 0:
+                        y = Fraction(0)
+                    ys.append(y)
+                ts, t = [], Fraction(0)
+                for j in range(T):
+                    t = rnd(t / 2 + ys[(j * K) // T])
+                    ts.append(t)
+                if T:
+                    r = ts[-1]
+                    for j in range(T - 2, -1, -1):
+                        r = rnd(ts[j] + r)
+                    acc = rnd(acc + r)
+            out[4 * lane + c] = acc
+    return out
+
+
+def test_fat_sink_identity_chain_closed_form():
+    """a = 1, b = 0: every y_s is ReLU(x), t_j = 2y(1 - 2^-(j+1)) and the
+    element's term is 2y(T - 1 + 2^-T).  x in {-1, 0, 1}: every value is exact
+    in fp32 at T = 16, so both evaluations equal the closed form bit for bit."""
+    rng = np.random.default_rng(5)
+    n, lanes, T, K = 4 * 37 + 3, 9, 16, 4
+    x = rng.integers(-1, 2, n).astype(np.float32)
+    a, b = np.ones(K, np.float32), np.zeros(K, np.float32)
+    term = 2.0 * (T - 1 + 2.0 ** -T)
+    expect = np.zeros(4 * lanes)
+    for q in range(n // 4):
+        expect[4 * (q % lanes): 4 * (q % lanes) + 4] += np.maximum(x[4 * q: 4 * q + 4], 0) * term
+    assert np.array_equal(oracle.chain_fat_sink_f64(x, a, b, True, T, lanes), expect)
+    assert np.array_equal(oracle.chain_fat_sink_f32(x, a, b, True, T, lanes).astype(np.float64), expect)
+    # without ReLU the negative elements count with their sign
+    expect_lin = np.zeros(4 * lanes)
+    for q in range(n // 4):
+        expect_lin[4 * (q % lanes): 4 * (q % lanes) + 4] += x[4 * q: 4 * q + 4] * term
+    assert np.array_equal(oracle.chain_fat_sink_f64(x, a, b, False, T, lanes), expect_lin)
+
+
+@pytest.mark.parametrize("K,T", [(4, 16), (4, 48), (3, 16), (8, 48), (4, 128)])
+def test_fat_sink_stage_mapping_closed_form(K, T):
+    """x = 0, a = 1, b_s distinct, no ReLU: y_s = b_0 + ... + b_s, and
+    sum_j t_j = sum_i y_{s(i)} * 2 (1 - 2^(i-T)) (a geometric sum in place of the
+    recurrence), which fixes which stage feeds which temporary."""
+    b = (np.arange(1, K + 1, dtype=np.float32) * np.float32(0.125)) ** 2
+    a = np.ones(K, np.float32)
+    x = np.zeros(4, np.float32)
+    ys = np.cumsum([Fraction(float(v)) for v in b])
+    total = sum(ys[(i * K) // T] * 2 * (1 - Fraction(2) ** (i - T)) for i in range(T))
+    got = oracle.chain_fat_sink_f64(x, a, b, False, T, 1)
+    assert np.all(np.abs(got - float(total)) <= 1e-13 * float(total))
+    got32 = oracle.chain_fat_sink_f32(x, a, b, False, T, 1).astype(np.float64)
+    assert np.all(np.abs(got32 - float(total)) <= 4 * T * 2.0 ** -24 * float(total))
+
+
+@pytest.mark.parametrize("K,T,relu,n,lanes", [(1, 16, True, 20, 2), (2, 16, True, 37, 3), (3, 16, False, 29, 1),
+                                              (4, 48, True, 40, 4), (4, 16, True, 13, 5)])
+def test_fat_sink_exact_rationals(K, T, relu, n, lanes):
+    """Against exact arithmetic: the fp64 sink within 1e-12 of the exact value
+    (relative to the sum of |t_j|); the fp32 sink bit for bit equal to exact
+    arithmetic rounded to fp32 after every step in the probe's order."""
+    x, a, b = synth.chain_inputs(n, K, salt=300 + 10 * K + T)
+    ex = _fat_sink_exact(x, a, b, relu, T, lanes)
+    got, absd = oracle.chain_fat_sink_f64(x, a, b, relu, T, lanes, with_abs=True)
+    for g, e, s in zip(got, ex, absd):
+        assert abs(Fraction(float(g)) - e) <= Fraction(1, 10**12) * (Fraction(float(s)) + 1)
+    ex32 = _fat_sink_exact(x, a, b, relu, T, lanes, round_each=True)
+    got32 = oracle.chain_fat_sink_f32(x, a, b, relu, T, lanes)
+    for g, e in zip(got32, ex32):
+        assert Fraction(float(g)) == e
+
+
+def test_fat_sink_lane_geometry_and_tail():
+    """One nonzero vector q lands in lane q mod L only; elements past the last
+    whole vector never reach the sink; T = 0 leaves the sink zero."""
+    K, T, lanes = 2, 16, 7
+    a, b = np.ones(K, np.float32), np.zeros(K, np.float32)
+    n = 4 * 50 + 3
+    for q in (0, 6, 7, 23, 49):
+        x = np.zeros(n, np.float32)
+        x[4 * q + 2] = 1.0
+        s = oracle.chain_fat_sink_f64(x, a, b, True, T, lanes)
+        nz = np.flatnonzero(s)
+        assert list(nz) == [4 * (q % lanes) + 2], (q, nz)
+    x = np.zeros(n, np.float32)
+    x[-3:] = 5.0
+    assert not oracle.chain_fat_sink_f64(x, a, b, True, T, lanes).any()
+    x, a2, b2 = synth.chain_inputs(n, K, salt=3)
+    assert not oracle.chain_fat_sink_f64(x, a2, b2, True, 0, lanes).any()
+    assert not oracle.chain_fat_sink_f32(x, a2, b2, True, 0, lanes).any()
+
+
+def test_fat_sink_f32_tracks_f64():
+    """At the probe's own geometry (2048 workgroups x 256 lanes, K = 4, T = 48)
+    on 1M elements: the fp32 sink is within 64 u of the fp64 one relative to
+    the sum of |t_j| (T + K + the lane's vectors roundings, each at most u of
+    that scale)."""
+    n, K, T, lanes = 1 << 20, 4, 48, 2048 * 256
+    x, a, b = synth.chain_inputs(n, K, salt=77)
+    s64, absd = oracle.chain_fat_sink_f64(x, a, b, True, T, lanes, with_abs=True)
+    s32 = oracle.chain_fat_sink_f32(x, a, b, True, T, lanes).astype(np.float64)
+    assert np.all(np.abs(s32 - s64) <= 64 * 2.0 ** -24 * absd + 1e-30)

@@ -116,3 +116,15 @@ def test_epilogue_large_positive_preactivation_passes_through():
     Y = oracle.gemm_epilogue_f64(A, B, bias, R)
     ref = 12.0 + (np.arange(N) * 0.25)[None, :] + np.arange(M * N).reshape(M, N) * 0.125
     assert np.max(np.abs(Y - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (17, 40, 24), (64, 128, 256), (130, 72, 520)])
+def test_matmul_form_equals_plain_form(M, N, K):
+    """The form that takes the product step from numpy's fp64 matmul (used at
+    4096^3, where the plain triple loop takes minutes) gives the plain
+    oracle's Y to fp64 rounding: the same bias, GELU and residual stages on a
+    product formed by a different routine."""
+    A, B, bias, R = synth.gemm_inputs(M, N, K, salt=400 + M)
+    plain = oracle.gemm_epilogue_f64(A, B, bias, R)
+    fast = oracle.gemm_epilogue_f64_matmul(A, B, bias, R)
+    assert np.max(np.abs(fast - plain) / (1 + np.abs(plain))) <= 1e-12

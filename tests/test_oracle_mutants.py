@@ -35,6 +35,18 @@ MUTANTS = [
      "test_oracle_chain.py"),
     ("chain-f32-relu-odd-stages", "oracle.c", "(s % 2) == 0 && v < 0.0f", "(s % 2) == 1 && v < 0.0f",
      "test_oracle_chain.py"),
+    # fat-probe sink ("C-05", section 3, fat row)
+    ("fat-sink-no-halving", "oracle.c", "t = 0.5 * t + y;", "t = t + y;", "test_oracle_chain.py"),
+    ("fat-sink-stage-modulo", "oracle.c", "for (; j < T && ((int64_t)j * K) / T == s; ++j) {\n                    t = 0.5",
+     "for (; j < T && (j % K) == s; ++j) {\n                    t = 0.5", "test_oracle_chain.py"),
+    ("fat-sink-lane-stride", "oracle.c", "q += lanes) {\n            double y", "q += 1) {\n            double y",
+     "test_oracle_chain.py"),
+    ("fat-sink-f32-forward-sum", "oracle.c",
+     "float r = t[T - 1];\n                        for (int jj = T - 2; jj >= 0; --jj)\n                            r = t[jj] + r;",
+     "float r = t[0];\n                        for (int jj = 1; jj < T; ++jj)\n                            r = r + t[jj];",
+     "test_oracle_chain.py"),
+    ("fat-sink-f32-two-roundings", "oracle.c", "y = fmaf(a[s], y, b[s]);\n                        if (relu_even",
+     "y = a[s] * y + b[s];\n                        if (relu_even", "test_oracle_chain.py"),
     # GEMM + bias + GELU + residual ("K4", section 1)
     ("gemm-b-transposed", "oracle.c", "half_bits_to_double(B[k * N + j])", "half_bits_to_double(B[j * K + k])",
      "test_oracle_gemm.py"),
