@@ -29,6 +29,7 @@ FC_ERR_UNSUPPORTED = -5
 FC_ERR_WORKSPACE = -6
 FC_ERR_HIP = -7
 FC_ERR_ALIAS = -8
+FC_ERR_SCRATCH = -9
 
 FC_CHAIN_NAIVE = 0
 FC_CHAIN_FUSED = 1
@@ -95,6 +96,7 @@ _SIGS = {
     "fc_chain_scratch_floats": (_SZ, [_I64, _I, _I, _I]),
     "fc_gemm_epilogue": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P, _SZ, _P]),
     "fc_gemm_workspace_bytes": (_SZ, [_I, _I, _I, _P, _I]),
+    "fc_gemm_epilogue_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
     "fc_causal_softmax": (_I, [_P, _P, _I64, _I, _F, _I, _I, _P, _SZ, _P]),
     "fc_causal_softmax_f32out": (_I, [_P, _P, _I64, _I, _F, _I, _P]),
     "fc_causal_softmax_tiles": (_I, [_P, _P, _P, _I64, _I, _F, _I, _P]),
@@ -276,6 +278,30 @@ def fc_gemm_epilogue(A, B, bias, R, Y, plan: Sequence[int], workspace=None, stre
     rc = _lib.fc_gemm_epilogue(_ptr(A), _ptr(B), _ptr(bias), _ptr(R), _ptr(Y), M, N, K, arr, n,
                                _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "fc_gemm_epilogue")
+
+
+# fixed scratch of fc_gemm_epilogue_noalloc (FC_GEMM_NOALLOC_SCRATCH_BYTES in fc.h)
+FC_GEMM_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fc_gemm_epilogue_noalloc(A, B, bias, R, Y, plan: Sequence[int], stream=None) -> None:
+    """fc_gemm_epilogue through the entry point that allocates nothing: the
+    library's own fixed per-device scratch holds the split-K partials and the
+    cut intermediate (calls needing more than FC_GEMM_NOALLOC_SCRATCH_BYTES
+    raise FcError(FC_ERR_SCRATCH)).  Calls that overlap in time on one device race."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (B, "B"), (bias, "bias"), (R, "R"), (Y, "Y")):
+        _dev(t, torch.float16, nm)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or bias.numel() != N or R.numel() != M * N or Y.numel() != M * N:
+        raise ValueError("shape mismatch")
+    arr, n = _int_array(plan)
+    rc = _lib.fc_gemm_epilogue_noalloc(_ptr(A), _ptr(B), _ptr(bias), _ptr(R), _ptr(Y), M, N, K, arr, n,
+                                       _stream(stream))
+    _check(rc, "fc_gemm_epilogue_noalloc")
 
 
 # ---------------------------------------------------------------- causal softmax

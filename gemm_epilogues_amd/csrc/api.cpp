@@ -199,6 +199,7 @@ extern "C" const char *fc_status_string(int status)
     case FC_ERR_WORKSPACE: return "workspace missing or too small";
     case FC_ERR_HIP: return "HIP launch failed";
     case FC_ERR_ALIAS: return "buffers overlap";
+    case FC_ERR_SCRATCH: return "needs more scratch than the library's fixed no-allocation array";
     default: return "unknown status";
     }
 }

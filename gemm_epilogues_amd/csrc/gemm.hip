@@ -24,6 +24,8 @@
 // across all banks.
 #include "fc_internal.h"
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 // The split-K handoffs of gemm_ring128_kernel and gemm_decode_kernel publish
@@ -1710,10 +1712,9 @@ extern "C" size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, 
     return inter_bytes(M, N, plan_len) + split_scratch_bytes(M, N, K);
 }
 
-extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
-                                const uint16_t *R, uint16_t *Y, int M, int N, int K,
-                                const int *plan, int plan_len, void *workspace, size_t ws_bytes,
-                                fc_stream stream)
+// Argument checks of both GEMM entry points; no HIP call.
+static int gemm_validate(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
+                         const uint16_t *Y, int M, int N, int K, const int *plan, int plan_len)
 {
     if (!plan_valid(plan, plan_len)) return FC_ERR_PLAN;
     if (M < 1 || N < 1 || K < 1) return FC_ERR_SHAPE;
@@ -1725,6 +1726,39 @@ extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint
     if (overlaps(Y, mn, A, (size_t)M * K * 2) || overlaps(Y, mn, B, (size_t)K * N * 2) ||
         overlaps(Y, mn, bias, (size_t)N * 2) || overlaps(Y, mn, R, mn))
         return FC_ERR_ALIAS;
+    return FC_OK;
+}
+
+// Enqueues the plan's kernels: the GEMM segment (split-K scratch in ds), then
+// the pointwise segments through the fp16 intermediate `inter`.
+static int gemm_enqueue(const uint16_t *A, const uint16_t *B, const uint16_t *bias, const uint16_t *R,
+                        uint16_t *Y, int M, int N, int K, const int *plan, int plan_len, DecodeScratch ds,
+                        uint16_t *inter, hipStream_t s)
+{
+    // operators: 0 = mm, 1 = bias, 2 = gelu, 3 = residual
+    int first = 0;
+    for (int seg = 0; seg < plan_len; ++seg) {
+        const int last = first + plan[seg] - 1;
+        uint16_t *dst = (seg == plan_len - 1) ? Y : inter;
+        int rc;
+        if (seg == 0)
+            rc = launch_gemm_segment(last, A, B, bias, R, dst, M, N, K, ds, s);
+        else
+            rc = launch_pointwise(first, last, inter, bias, R, dst, (int64_t)M * N, N, s);
+        if (rc != FC_OK) return rc;
+        first = last + 1;
+    }
+    return FC_OK;
+}
+
+extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                                const uint16_t *R, uint16_t *Y, int M, int N, int K,
+                                const int *plan, int plan_len, void *workspace, size_t ws_bytes,
+                                fc_stream stream)
+{
+    const int v = gemm_validate(A, B, bias, R, Y, M, N, K, plan, plan_len);
+    if (v != FC_OK) return v;
+    const size_t mn = (size_t)M * N * 2;
     const size_t need = fc_gemm_workspace_bytes(M, N, K, plan, plan_len);
     size_t counter_bytes, partial_bytes;
     split_scratch(M, N, K, counter_bytes, partial_bytes);
@@ -1744,19 +1778,80 @@ extern "C" int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint
             ds.partials = reinterpret_cast<float *>(base + counter_bytes);
         }
     }
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // operators: 0 = mm, 1 = bias, 2 = gelu, 3 = residual
-    int first = 0;
-    for (int seg = 0; seg < plan_len; ++seg) {
-        const int last = first + plan[seg] - 1;
-        uint16_t *dst = (seg == plan_len - 1) ? Y : ws;
-        int rc;
-        if (seg == 0)
-            rc = launch_gemm_segment(last, A, B, bias, R, dst, M, N, K, ds, s);
-        else
-            rc = launch_pointwise(first, last, ws, bias, R, dst, (int64_t)M * N, N, s);
-        if (rc != FC_OK) return rc;
-        first = last + 1;
+    return gemm_enqueue(A, B, bias, R, Y, M, N, K, plan, plan_len, ds, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+
+// The workspace of fc_gemm_epilogue_noalloc: one array per device, held until
+// the process ends.  Host code never uses its name as an address (on the host
+// the name is a stand-in, not the device allocation): the device address is
+// looked up once per device and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[FC_GEMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];   // device address of `scratch` on device d, once looked up
+}  // namespace
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+static int scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FC_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FC_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return FC_ERR_HIP;
+        }
+        scratch_ptr[dev] = p;
     }
+    *out = scratch_ptr[dev];
     return FC_OK;
+}
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, int64_t words)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+extern "C" int fc_gemm_epilogue_noalloc(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                                        const uint16_t *R, uint16_t *Y, int M, int N, int K,
+                                        const int *plan, int plan_len, fc_stream stream)
+{
+    const int v = gemm_validate(A, B, bias, R, Y, M, N, K, plan, plan_len);
+    if (v != FC_OK) return v;
+    const size_t need = fc_gemm_workspace_bytes(M, N, K, plan, plan_len);
+    if (need > FC_GEMM_NOALLOC_SCRATCH_BYTES) return FC_ERR_SCRATCH;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *base = nullptr;
+    if (need) {
+        void *p = nullptr;
+        const int rc = scratch_on_current_device(&p);
+        if (rc != FC_OK) return rc;
+        base = static_cast<char *>(p);
+    }
+    size_t counter_bytes, partial_bytes;
+    split_scratch(M, N, K, counter_bytes, partial_bytes);
+    DecodeScratch ds = {nullptr, nullptr};
+    if (counter_bytes) {
+        // the previous call on this device may have left anything here (another
+        // shape's partials or intermediate): the arrival counters start at zero
+        ds.counters = reinterpret_cast<uint32_t *>(base);
+        ds.partials = reinterpret_cast<float *>(base + counter_bytes);
+        const int64_t words = (int64_t)(counter_bytes / 4);
+        zero_words_kernel<<<(int)std::min<int64_t>(64, ceil_div(words, (int64_t)256)), 256, 0, s>>>(ds.counters,
+                                                                                                  words);
+        const int rc = launch_status();
+        if (rc != FC_OK) return rc;
+    }
+    uint16_t *inter = need ? reinterpret_cast<uint16_t *>(base + counter_bytes + partial_bytes) : nullptr;
+    return gemm_enqueue(A, B, bias, R, Y, M, N, K, plan, plan_len, ds, inter, s);
 }

@@ -38,7 +38,9 @@ enum {
     FC_ERR_UNSUPPORTED = -5,  /* valid but unsupported (K stages, tile, temps...) */
     FC_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required       */
     FC_ERR_HIP = -7,          /* a HIP launch failed                              */
-    FC_ERR_ALIAS = -8         /* buffers overlap where they must not              */
+    FC_ERR_ALIAS = -8,        /* buffers overlap where they must not              */
+    FC_ERR_SCRATCH = -9       /* a no-allocation call needs more scratch than the
+                                 library's fixed array holds                      */
 };
 
 enum { FC_CHAIN_NAIVE = 0, FC_CHAIN_FUSED = 1, FC_CHAIN_FAT = 2 };
@@ -154,6 +156,34 @@ int fc_gemm_epilogue(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
  *    D = round_up(4*T, 256) + 65536*T*P when P > 1.
  * 0 for an invalid plan or shape (fc_gemm_epilogue then returns an error). */
 size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_len);
+
+/*
+ * fc_gemm_epilogue_noalloc -- fc_gemm_epilogue without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * allocates nothing and calls no allocating routine: the split-K scratch and
+ * the fp16 intermediate of a cut plan live in a fixed array of
+ * FC_GEMM_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device,
+ * held until the process ends.  Same kernels, same results as
+ * fc_gemm_epilogue (bit for bit) and the same arguments without workspace and
+ * ws_bytes.
+ *
+ *  Limit: calls whose fc_gemm_workspace_bytes(M, N, K, plan) exceeds
+ *  FC_GEMM_NOALLOC_SCRATCH_BYTES return FC_ERR_SCRATCH before anything is
+ *  launched (e.g. any plan with a cut needs 2*M*N bytes for its intermediate,
+ *  so M*N <= 32M elements less the split scratch).
+ *  Every call on a device shares that device's array: the call clears the
+ *  arrival counters it needs (a small fill kernel on `stream`, no memset) and
+ *  overwrites the rest, so back-to-back calls of any shapes need nothing from
+ *  the caller, but calls that overlap in time on one device (different
+ *  streams or host threads without ordering) race and give undefined results.
+ *  The first call on a device looks the array's address up with that device
+ *  current (FC_ERR_HIP if that fails).  Other errors as fc_gemm_epilogue.
+ */
+#define FC_GEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fc_gemm_epilogue_noalloc(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                             const uint16_t *R, uint16_t *Y, int M, int N, int K,
+                             const int *plan, int plan_len, fc_stream stream);
 
 /* ---------------------------------------------------- causal softmax */
 
