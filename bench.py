@@ -677,6 +677,9 @@ def main():
                          "fat sweep, all split plans, graph replay) timed after the steps")
     ap.add_argument("--no-torch-rows", action="store_true",
                     help="skip the PyTorch eager (unfused library) rows timed after the steps")
+    ap.add_argument("--min-row-samples", type=int, default=MIN_ROW_SAMPLES,
+                    help="event pairs per row at least: steps beyond --steps are run after the timed "
+                         "region for the per-row medians (0: only the timed steps, e.g. under counters)")
     ap.add_argument("--graph", action="store_true",
                     help="time each row as one replay of a HIP graph captured from its calls")
     args = ap.parse_args()
@@ -900,7 +903,7 @@ def main():
     # more samples per row after the timed region, so that every row's median
     # and minimum come from at least MIN_ROW_SAMPLES event pairs (value and
     # ms_per_step stay those of the timed steps)
-    extra_steps = max(0, MIN_ROW_SAMPLES - args.steps)
+    extra_steps = max(0, args.min_row_samples - args.steps)
     if extra_steps:
         log(f"sampling {extra_steps} more steps per row")
         for i in range(extra_steps):

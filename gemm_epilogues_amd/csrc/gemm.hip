@@ -1393,20 +1393,25 @@ __global__ __launch_bounds__(dec::NT, 1) void gemm_decode_kernel(
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
         if (t < nsteps) {
+            // all 8 fragment reads of the k-step first, one wait: lane i of
+            // group g addresses k-row 32t + 8g + 4hh + i/4, columns 16j +
+            // 4(i%4) .. +3; the transposing read hands lane i column 16j + i
+            // at four consecutive k
+            u32x2 bh[4][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // lane i of group g addresses k-row 32t + 8g + 4hh + i/4,
-                // columns 16j + 4(i%4) .. +3; the transposing read hands
-                // lane i column 16j + i at four consecutive k
-                u32x2 bh[2];
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int k = dec::KSTEP * t + 8 * g + 4 * hh + (i >> 2);
-                    bh[hh] = lds_read_tr16(slab0 + k * dec::ROW +
-                                           16 * ((2 * j + ((i & 3) >> 1)) ^ dec_swz(k)) + (i & 1) * 8);
+                    bh[j][hh] = lds_read_tr16(slab0 + k * dec::ROW +
+                                              16 * ((2 * j + ((i & 3) >> 1)) ^ dec_swz(k)) + (i & 1) * 8);
                 }
-                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bh[0]), "+v"(bh[1]));
-                const u32x4 bq = {bh[0].x, bh[0].y, bh[1].x, bh[1].y};
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(bh[0][0]), "+v"(bh[0][1]), "+v"(bh[1][0]), "+v"(bh[1][1]), "+v"(bh[2][0]),
+                           "+v"(bh[2][1]), "+v"(bh[3][0]), "+v"(bh[3][1]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 bq = {bh[j][0].x, bh[j][0].y, bh[j][1].x, bh[j][1].y};
 #pragma unroll
                 for (int rb = 0; rb < MB; ++rb)
                     acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[rb][t], __builtin_bit_cast(f16x8, bq),
