@@ -764,9 +764,10 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
         // once, and R loads and Y stores of 16 bytes, a wave covering two
         // 512-byte row pieces per instruction (in the accumulator layout a
         // wave's 8-byte accesses touch 32 rows each).  LDS: row r at r * 1 KiB,
-        // 16-byte unit u at u ^ (r & 63), so the writes (32 rows, one unit) and
-        // the reads (one row, 32 units) are both conflict-free.  Same
-        // arithmetic per element as the accumulator-layout path.
+        // 16-byte unit u at u ^ ((u >> 4) & 1) ^ (r & 63): 16 lanes writing one
+        // unit of 16 rows, or reading units 2c (or 2c + 1) of one row, cover all
+        // 16 bank groups (no conflicts).  Same arithmetic per element as the
+        // accumulator-layout path.
         __syncthreads();                         // every wave is done with the ring
         FC_LDS float *sh = (FC_LDS float *)lds;
         const int rl = lane >> 5, cu = lane & 31;
@@ -799,15 +800,16 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
                             const int u = 16 * wn + 8 * j + 2 * g + rl;
                             const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                              acc[i][j][4 * g + 3]};
-                            *(FC_LDS f32x4 *)(sh + r * 256 + ((u ^ (r & 63)) << 2)) = v;
+                            *(FC_LDS f32x4 *)(sh + r * 256 + ((u ^ ((u >> 4) & 1) ^ (r & 63)) << 2)) = v;
                         }
             }
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int r = q * 16 + 2 * wave + rl;
-                const f32x4 x0 = *(const FC_LDS f32x4 *)(sh + r * 256 + (((2 * cu) ^ (r & 63)) << 2));
-                const f32x4 x1 = *(const FC_LDS f32x4 *)(sh + r * 256 + (((2 * cu + 1) ^ (r & 63)) << 2));
+                const int u0 = 2 * cu, u1 = 2 * cu + 1;
+                const f32x4 x0 = *(const FC_LDS f32x4 *)(sh + r * 256 + ((u0 ^ ((u0 >> 4) & 1) ^ (r & 63)) << 2));
+                const f32x4 x1 = *(const FC_LDS f32x4 *)(sh + r * 256 + ((u1 ^ ((u1 >> 4) & 1) ^ (r & 63)) << 2));
                 u32x4 y;
                 y.x = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x0.x, bv[0], f16_lo(rw[q].x)),
                                      apply_ops<OP_BIAS, LAST>(x0.y, bv[1], f16_hi(rw[q].x)));
