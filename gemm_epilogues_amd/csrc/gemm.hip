@@ -1143,10 +1143,64 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
         if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Epilogue on the accumulators (C^T layout: lane owns row m = lane % 32 of
-    // tile row i and columns 8g + 4*(lane/32) .. +3 of tile column j), laid
-    // out as the 256x256 kernel's: bias converted once, interior tiles through
-    // one row pointer with constant column offsets.
+    if (m0 + r128::BM <= M && n0 + r128::BN <= N) {
+        // Interior tile: as the 256x256 kernel, the accumulators pass through
+        // the freed ring (the whole 128x128 fp32 tile, 64 KiB, one pass) into a
+        // row-major layout; a lane then finishes 8 consecutive columns of a
+        // row with 16-byte R loads and Y stores.  Row r at r * 512 bytes,
+        // 16-byte unit u at u ^ ((u >> 4) & 1) ^ (r & 31) (no bank conflicts).
+        __syncthreads();                         // every wave is done with the ring
+        FC_LDS float *sh = (FC_LDS float *)lds;
+        const int rq = threadIdx.x >> 4, cu = threadIdx.x & 15;   // 16 rows x 16 lanes per pass of q
+        const int col = 8 * cu;
+        float bv[8];
+        {
+            u32x4 bw = {0u, 0u, 0u, 0u};
+            if (LAST >= OP_BIAS) bw = *reinterpret_cast<const u32x4 *>(bias + n0 + col);
+            bv[0] = f16_lo(bw.x); bv[1] = f16_hi(bw.x); bv[2] = f16_lo(bw.y); bv[3] = f16_hi(bw.y);
+            bv[4] = f16_lo(bw.z); bv[5] = f16_hi(bw.z); bv[6] = f16_lo(bw.w); bv[7] = f16_hi(bw.w);
+        }
+        const int64_t rbase = (int64_t)(m0 + rq) * N + n0 + col;
+        u32x4 rw[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            rw[q] = u32x4{0u, 0u, 0u, 0u};
+            if (LAST >= OP_RES) rw[q] = *reinterpret_cast<const u32x4 *>(R + rbase + (int64_t)q * 16 * N);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int r = wm * 64 + 32 * i + (lane & 31);
+                    const int u = 16 * wn + 8 * j + 2 * g + (lane >> 5);
+                    const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    *(FC_LDS f32x4 *)(sh + r * 128 + ((u ^ ((u >> 4) & 1) ^ (r & 31)) << 2)) = v;
+                }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = q * 16 + rq;
+            const int u0 = 2 * cu, u1 = 2 * cu + 1;
+            const f32x4 x0 = *(const FC_LDS f32x4 *)(sh + r * 128 + ((u0 ^ ((u0 >> 4) & 1) ^ (r & 31)) << 2));
+            const f32x4 x1 = *(const FC_LDS f32x4 *)(sh + r * 128 + ((u1 ^ ((u1 >> 4) & 1) ^ (r & 31)) << 2));
+            u32x4 y;
+            y.x = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x0.x, bv[0], f16_lo(rw[q].x)),
+                                 apply_ops<OP_BIAS, LAST>(x0.y, bv[1], f16_hi(rw[q].x)));
+            y.y = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x0.z, bv[2], f16_lo(rw[q].y)),
+                                 apply_ops<OP_BIAS, LAST>(x0.w, bv[3], f16_hi(rw[q].y)));
+            y.z = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x1.x, bv[4], f16_lo(rw[q].z)),
+                                 apply_ops<OP_BIAS, LAST>(x1.y, bv[5], f16_hi(rw[q].z)));
+            y.w = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x1.z, bv[6], f16_lo(rw[q].w)),
+                                 apply_ops<OP_BIAS, LAST>(x1.w, bv[7], f16_hi(rw[q].w)));
+            *reinterpret_cast<u32x4 *>(out + rbase + (int64_t)q * 16 * N) = y;
+        }
+        return;
+    }
+    // Tiles with an M or N tail: straight from the accumulators (C^T layout:
+    // lane owns row m = lane % 32 of tile row i and columns 8g + 4*(lane/32)
+    // .. +3 of tile column j), every store checked.
     float bf[2][4][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -1168,23 +1222,6 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
                              apply_ops<OP_BIAS, LAST>(acc[i][j][4 * g + 3], bf[j][g][3], f16_hi(rw.y)));
         return y;
     };
-    if (m0 + r128::BM <= M && n0 + r128::BN <= N) {
-        const int64_t base = (int64_t)(m0 + wm * 64 + (lane & 31)) * N + n0 + wn * 64 + 4 * (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint16_t *Rr = R + base + (int64_t)i * 32 * N;
-            uint16_t *Yr = out + base + (int64_t)i * 32 * N;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 rw = {0u, 0u};
-                    if (LAST >= OP_RES) rw = *reinterpret_cast<const u32x2 *>(Rr + j * 32 + 8 * g);
-                    *reinterpret_cast<u32x2 *>(Yr + j * 32 + 8 * g) = out4(i, j, g, rw);
-                }
-        }
-        return;
-    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int m = m0 + wm * 64 + i * 32 + (lane & 31);
