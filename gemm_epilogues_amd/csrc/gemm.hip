@@ -1892,12 +1892,21 @@ void *scratch_ptr[kMaxDevices];   // device address of `scratch` on device d, on
 }  // namespace
 
 // Device address of `scratch` on the current device (looked up on the first
-// call on that device, with that device current).
-static int scratch_on_current_device(void **out)
+// call on that device, with that device current).  A stream of another
+// device would run the kernels against this device's array: refused.
+static int scratch_on_current_device(hipStream_t stream, void **out)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return FC_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return FC_ERR_UNSUPPORTED;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return FC_ERR_HIP;
+        }
+        if (sdev != dev) return FC_ERR_UNSUPPORTED;
+    }
     std::lock_guard<std::mutex> lock(scratch_mu);
     if (!scratch_ptr[dev]) {
         void *p = nullptr;
@@ -1930,7 +1939,7 @@ extern "C" int fc_gemm_epilogue_noalloc(const uint16_t *A, const uint16_t *B, co
     char *base = nullptr;
     if (need) {
         void *p = nullptr;
-        const int rc = scratch_on_current_device(&p);
+        const int rc = scratch_on_current_device(s, &p);
         if (rc != FC_OK) return rc;
         base = static_cast<char *>(p);
     }

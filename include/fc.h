@@ -177,7 +177,9 @@ size_t fc_gemm_workspace_bytes(int M, int N, int K, const int *plan, int plan_le
  *  overwrites the rest, so back-to-back calls of any shapes need nothing from
  *  the caller, but calls that overlap in time on one device (different
  *  streams or host threads without ordering) race and give undefined results.
- *  The first call on a device looks the array's address up with that device
+ *  The array used is the current device's: `stream` must belong to the
+ *  current device (FC_ERR_UNSUPPORTED otherwise, before any launch).  The
+ *  first call on a device looks the array's address up with that device
  *  current (FC_ERR_HIP if that fails).  Other errors as fc_gemm_epilogue.
  */
 #define FC_GEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
