@@ -57,6 +57,21 @@ __global__ __launch_bounds__(kBlock) void mix_kernel(const f32x4 *__restrict__ s
     }
 }
 
+// Flat streams: one 16-byte vector per lane, one 4 KiB workgroup per 256
+// vectors, a grid that covers the buffer once (the fastest plain write and
+// copy shape measured on this device: each workgroup's footprint is small).
+__global__ __launch_bounds__(kBlock) void flat_write_kernel(f32x4 *__restrict__ dst)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    dst[i] = f32x4{1.0f, 2.0f, 3.0f, (float)threadIdx.x};
+}
+
+__global__ __launch_bounds__(kBlock) void flat_copy_kernel(const f32x4 *__restrict__ src, f32x4 *__restrict__ dst)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 __global__ __launch_bounds__(kBlock) void read_kernel(const f32x4 *__restrict__ src, float *__restrict__ sink)
 {
     const f32x4 *in = src + (int64_t)blockIdx.x * (kBlock * kVecs) + threadIdx.x;
@@ -138,6 +153,25 @@ extern "C" int fce_mix(const void *src, size_t read_bytes, void *dst, size_t wri
         mix_kernel<1><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
     else
         mix_kernel<2><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
+    return fc::launch_status();
+}
+
+// Flat granule: 256 lanes x 16 bytes.
+static constexpr size_t kFlat = (size_t)kBlock * 16;
+
+extern "C" int fce_flat(const void *src, void *dst, size_t bytes, fc_stream stream)
+{
+    if (!dst) return FC_ERR_NULL;
+    if (bytes == 0 || bytes % kFlat) return FC_ERR_SHAPE;
+    if (!fc::aligned16(src) || !fc::aligned16(dst)) return FC_ERR_ALIGN;
+    if (src && fc::overlaps(src, bytes, dst, bytes)) return FC_ERR_ALIAS;
+    const int64_t blocks = (int64_t)(bytes / kFlat);
+    if (blocks > 0x7fffffff) return FC_ERR_UNSUPPORTED;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (src)
+        flat_copy_kernel<<<(unsigned)blocks, kBlock, 0, s>>>(static_cast<const f32x4 *>(src), static_cast<f32x4 *>(dst));
+    else
+        flat_write_kernel<<<(unsigned)blocks, kBlock, 0, s>>>(static_cast<f32x4 *>(dst));
     return fc::launch_status();
 }
 

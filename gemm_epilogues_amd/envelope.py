@@ -22,13 +22,14 @@ _P, _SZ, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 _lib.fce_chunk_bytes.restype, _lib.fce_chunk_bytes.argtypes = _SZ, []
 _lib.fce_mix.restype, _lib.fce_mix.argtypes = _I, [_P, _SZ, _P, _SZ, _P]
 _lib.fce_read.restype, _lib.fce_read.argtypes = _I, [_P, _SZ, _P, _P]
+_lib.fce_flat.restype, _lib.fce_flat.argtypes = _I, [_P, _P, _SZ, _P]
 _lib.fce_mfma.restype, _lib.fce_mfma.argtypes = _I, [_P, _I, _P]
 _lib.fce_mfma_sink_floats.restype, _lib.fce_mfma_sink_floats.argtypes = _SZ, []
 _lib.fce_mfma_flops.restype, _lib.fce_mfma_flops.argtypes = ctypes.c_double, [_I]
 _lib.fce_empty.restype, _lib.fce_empty.argtypes = _I, [_I, _P, _P]
 
-EXPORTED = ("fce_chunk_bytes", "fce_mix", "fce_read", "fce_mfma", "fce_mfma_sink_floats", "fce_mfma_flops",
-            "fce_empty")
+EXPORTED = ("fce_chunk_bytes", "fce_mix", "fce_read", "fce_flat", "fce_mfma", "fce_mfma_sink_floats",
+            "fce_mfma_flops", "fce_empty")
 
 
 def _addr(t):
@@ -54,6 +55,12 @@ def fce_mix(src, read_bytes: int, dst, write_bytes: int, stream=None) -> None:
 
 def fce_read(src, read_bytes: int, sink, stream=None) -> None:
     fc._check(_lib.fce_read(_addr(src), int(read_bytes), _addr(sink), _stream(stream)), "fce_read")
+
+
+def fce_flat(src, dst, nbytes: int, stream=None) -> None:
+    """Flat stream of nbytes: a pure write of dst when src is None, else a copy."""
+    fc._check(_lib.fce_flat(_addr(src) if src is not None else None, _addr(dst), int(nbytes), _stream(stream)),
+              "fce_flat")
 
 
 def fce_mfma_sink_floats() -> int:

@@ -36,6 +36,17 @@ size_t fce_chunk_bytes(void);
  */
 int fce_mix(const void *src, size_t read_bytes, void *dst, size_t write_bytes, fc_stream stream);
 
+/*
+ * fce_flat -- a flat stream of `bytes` (a multiple of 4 KiB) in the shape
+ * with the smallest workgroup footprint: one 16-byte vector per lane, one
+ * 4 KiB workgroup per 256 vectors, a grid that covers the buffer once.  With
+ * src == NULL it writes a constant to dst (a pure write); otherwise it copies
+ * src to dst with nontemporal loads and stores.  Errors: FC_ERR_NULL (dst),
+ * FC_ERR_SHAPE, FC_ERR_ALIGN, FC_ERR_ALIAS, FC_ERR_UNSUPPORTED (beyond 2^31
+ * workgroups).
+ */
+int fce_flat(const void *src, void *dst, size_t bytes, fc_stream stream);
+
 /* fce_read -- read `read_bytes` (whole chunks) of device buffer src; sink is
  * a device float that is written only for one impossible data pattern. */
 int fce_read(const void *src, size_t read_bytes, float *sink, fc_stream stream);

@@ -58,3 +58,22 @@ def test_read_and_mfma_probes_run():
     torch.cuda.synchronize()
     assert sink.item() == 7.0
     assert torch.isfinite(msink).all() and torch.equal(a, msink) and msink.abs().sum() > 0
+
+
+def test_flat_streams():
+    """fce_flat copies src to dst exactly, or writes its constant pattern
+    (1, 2, 3, lane) per 16 bytes over the whole buffer."""
+    announce("envelope flat streams")
+    dev = torch.device("cuda", 0)
+    nbytes = 37 * 4096
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    dst = torch.zeros_like(src)
+    env.fce_flat(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    env.fce_flat(None, dst, nbytes)
+    torch.cuda.synchronize()
+    d = dst.view(torch.float32).cpu().numpy().reshape(-1, 4)
+    lane = np.arange(d.shape[0]) % 256
+    assert np.array_equal(d, np.stack([np.full(lane.size, 1.0), np.full(lane.size, 2.0), np.full(lane.size, 3.0),
+                                       lane.astype(np.float64)], 1).astype(np.float32))
