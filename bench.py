@@ -678,7 +678,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the timed oracle sample on the host cores (the parity checks against the "
+                         "oracle before the timed steps always run)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one plain 1 GiB device copy before the timed region (a known-size "
                          "kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")

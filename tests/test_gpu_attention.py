@@ -64,23 +64,22 @@ def test_small_shapes_all_rows(BH, S):
     assert ok, worst
 
 
-def test_full_config_sampled_rows():
+def test_full_config_every_row():
     """[8*16, 2048, 128] (the softmax workload's heads and length, head dim 128):
-    rows at tile edges and random rows of three heads against the oracle."""
-    BH, S = 128, 2048
-    announce(f"attention full config BH={BH} S={S} sampled rows")
-    Q, K, V = synth.attention_inputs(BH, S, 128)
-    out = run(Q, K, V).reshape(BH * S, 128)
-    rng = np.random.default_rng(1)
-    edges = [0, 1, 31, 32, 63, 64, 127, 128, 129, 1023, 1024, 2046, 2047]
-    rows = []
-    for h in (0, 77, 127):
-        rows += [h * S + i for i in edges] + list(h * S + rng.integers(0, S, 40))
-    rows = np.array(rows)
-    ref = oracle.causal_attention_rows(Q, K, V, SCALE, rows)
-    cm = colmax_prefix(V).reshape(BH * S, 128)[rows]
-    ok, worst = check(out[rows], ref, cm)
-    assert ok, worst
+    every output row against the oracle, 16 heads at a time."""
+    BH, S, D = 128, 2048, 128
+    announce(f"attention full config BH={BH} S={S} every row")
+    Q, K, V = synth.attention_inputs(BH, S, D)
+    out = run(Q, K, V)
+    worst = 0.0
+    for h0 in range(0, BH, 16):
+        h1 = min(BH, h0 + 16)
+        ref = oracle.causal_attention_rows(Q[h0:h1], K[h0:h1], V[h0:h1], SCALE,
+                                           np.arange((h1 - h0) * S)).reshape(h1 - h0, S, D)
+        ok, w = check(out[h0:h1], ref, colmax_prefix(V[h0:h1]))
+        assert ok, (h0, w)
+        worst = max(worst, w)
+    announce(f"  worst error / bound = {worst:.3f}")
 
 
 def test_closed_forms_on_the_gpu():
@@ -104,15 +103,14 @@ def test_deterministic():
     assert np.array_equal(run(Q, K, V), run(Q, K, V))
 
 
-def test_long_sequence_sampled_rows():
-    """S = 4096 (64 key tiles for the last query tile), one head."""
+def test_long_sequence_every_row():
+    """S = 4096 (64 key tiles for the last query tile), one head, every row."""
     S = 4096
     announce(f"attention long sequence S={S}")
     Q, K, V = synth.attention_inputs(1, S, 128, salt=41)
-    out = run(Q, K, V).reshape(S, 128)
-    rows = np.array([0, 1, 127, 128, 2047, 2048, 4094, 4095])
-    ref = oracle.causal_attention_rows(Q, K, V, SCALE, rows)
-    ok, worst = check(out[rows], ref, colmax_prefix(V).reshape(S, 128)[rows])
+    out = run(Q, K, V)
+    ref = oracle.causal_attention_f64(Q, K, V, SCALE)
+    ok, worst = check(out, ref, colmax_prefix(V))
     assert ok, worst
 
 
