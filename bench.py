@@ -669,6 +669,19 @@ def measure_torch_rows(torch, stream, groups, bufs):
             p = torch.softmax(s.masked_fill(mask, float("-inf")), -1).to(torch.bfloat16)
             return torch.matmul(p, va)
         out["attention_us"] = round(_median_ms(torch, stream, att, 1, iters=3) * 1e3, 2)
+        # the vendor's fused attention (torch SDPA restricted to its flash
+        # backend: where that backend cannot run, the call raises instead of
+        # falling back to the score-materialising math path)
+        try:
+            from torch.nn.attention import sdpa_kernel, SDPBackend
+            BH, D = qa.shape[0], qa.shape[-1]
+            q4, k4, v4 = (x.view(BH // 16, 16, S, D) for x in (qa, ka, va))
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                out["attention_sdpa_flash_us"] = round(_median_ms(
+                    torch, stream, lambda r: F.scaled_dot_product_attention(q4, k4, v4, is_causal=True, scale=SCALE),
+                    1, iters=11) * 1e3, 2)
+        except Exception as ex:  # backend missing on this build: no figure
+            out["attention_sdpa_flash_error"] = f"{type(ex).__name__}: {str(ex)[:120]}"
     torch.cuda.synchronize()
     return out
 
@@ -1105,7 +1118,8 @@ def main():
     if torch_rows:
         pairs = {"chain_K8_us": ("chain_K8", "fused_us"), "decode_us": ("decode_plan4", "us"),
                  "gemm_4096_us": ("gemm_plan4", "us"), "softmax_us": ("softmax_fused_T64", "us"),
-                 "attention_us": ("attention_fused", "us"), "rmsnorm_us": ("rmsnorm_1024x4096", "fused_us")}
+                 "attention_us": ("attention_fused", "us"), "attention_sdpa_flash_us": ("attention_fused", "us"),
+                 "rmsnorm_us": ("rmsnorm_1024x4096", "fused_us")}
         for k, (row, f) in pairs.items():
             if k in torch_rows and row in comp:
                 torch_rows[k.replace("_us", "_speedup_fused_vs_torch")] = round(torch_rows[k] / comp[row][f], 2)

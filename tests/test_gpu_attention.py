@@ -154,3 +154,20 @@ def test_wide_dynamic_range(case):
     ref = oracle.causal_attention_f64(Q, K, V, scale)
     ok, worst = check(out, ref, colmax_prefix(V))
     assert ok, worst
+
+
+def random_attention_shapes():
+    rng = np.random.default_rng(20261002 + 2)
+    return [(int(rng.integers(1, 6)), int(rng.integers(1, 900))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("BH,S", random_attention_shapes())
+def test_random_shapes_all_rows(BH, S):
+    """Seeded random head counts and sequence lengths (ragged query and key
+    tiles): every output row against the oracle."""
+    announce(f"attention random shape BH={BH} S={S}")
+    Q, K, V = synth.attention_inputs(BH, S, 128, salt=BH * 7919 + S)
+    out = run(Q, K, V)
+    ref = oracle.causal_attention_f64(Q, K, V, SCALE)
+    ok, worst = check(out, ref, colmax_prefix(V))
+    assert ok, worst

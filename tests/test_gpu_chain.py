@@ -178,3 +178,24 @@ def test_fat_probe_full_size(full_chain_inputs, K, temps):
     announce(f"fat full size n=16777216 K={K} temps={temps}")
     x, a, b, xd = full_chain_inputs(K)
     check_fat(x, a, b, True, temps, xd)
+
+
+def random_chain_cases():
+    rng = np.random.default_rng(20261002 + 4)
+    return [(int(rng.integers(1, 400000)), int(rng.integers(1, 33)), bool(rng.integers(0, 2))) for _ in range(10)]
+
+
+@pytest.mark.parametrize("n,K,relu", random_chain_cases())
+def test_random_lengths_and_stage_counts(n, K, relu):
+    """Seeded random lengths (ragged tails) and stage counts 1..32: naive and
+    fused equal the oracle's one-rounding chain bit for bit, and the fat probe
+    (where it supports K) its y and sink."""
+    announce(f"chain random n={n} K={K} relu={relu}")
+    x, a, b = synth.chain_inputs(n, K, salt=n + K)
+    ref32 = oracle.chain_f32fma(x, a, b, relu)
+    xd = f32(x)
+    for mode in (fc.FC_CHAIN_NAIVE, fc.FC_CHAIN_FUSED):
+        y, _ = run(xd, a, b, relu, mode)
+        assert np.array_equal(y, ref32), mode
+    if K in (1, 2, 3, 4, 6, 8):
+        check_fat(x, a, b, relu, 48, xd)

@@ -342,3 +342,28 @@ def test_side_stream_without_workspace(M, N, K):
             ok, worst = tol_ok(y, ref)
             assert ok, (plan, worst)
             assert np.array_equal(y, base), plan
+
+
+def random_shapes():
+    """Seeded shapes for each kernel route: split-K decode (M <= 64, N % 64 = 0,
+    K % 256 = 0), the M <= 16 kernel without a decode split (K % 256 != 0),
+    the 128x128 ring (K % 64 = 0), the register-staged kernels (K % 64 != 0)
+    and the 256x256 ring (more than 512 tiles of 128x128)."""
+    rng = np.random.default_rng(20261002)
+    out = []
+    for _ in range(5):
+        out.append((int(rng.integers(1, 65)), 64 * int(rng.integers(1, 20)), 256 * int(rng.integers(1, 5))))
+        out.append((int(rng.integers(1, 17)), 8 * int(rng.integers(1, 150)), 8 * int(rng.integers(1, 128)) | 8))
+        out.append((int(rng.integers(65, 700)), 8 * int(rng.integers(1, 150)), 64 * int(rng.integers(1, 17))))
+        out.append((int(rng.integers(17, 700)), 8 * int(rng.integers(1, 150)), 8 * int(rng.integers(1, 128)) | 8))
+    for _ in range(2):
+        out.append((int(rng.integers(2049, 2400)), 8 * int(rng.integers(513, 640)), 64 * int(rng.integers(1, 4))))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes())
+def test_random_shapes_every_output(M, N, K):
+    """Every output of all eight plans against the oracle on seeded random
+    shapes that reach every kernel route, ragged edges included."""
+    announce(f"gemm random shape {M}x{N}x{K}")
+    check_every_output(Dev(M, N, K, salt=M + N + K), ALL_PLANS)

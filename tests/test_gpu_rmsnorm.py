@@ -85,3 +85,20 @@ def test_unfused_on_a_side_stream_without_workspace():
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         assert np.array_equal(yd.cpu().numpy(), base)
+
+
+def random_rmsnorm_shapes():
+    rng = np.random.default_rng(20261002 + 3)
+    return [(int(rng.integers(1, 300)), 4 * int(rng.integers(1, 4097))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("rows,d", random_rmsnorm_shapes())
+def test_random_shapes_both_forms(rows, d):
+    """Seeded random row counts and widths (any multiple of 4 up to 16384):
+    both forms against the oracle."""
+    announce(f"rmsnorm random shape rows={rows} d={d}")
+    x, g = inputs(rows, d, rows * 7 + d)
+    ref = oracle.rmsnorm_f64(x, g, 1e-5)
+    for mode in (0, 1):
+        y = run(x, g, 1e-5, mode).astype(np.float64)
+        assert np.all(np.abs(y - ref) <= 4e-6 * np.abs(ref)), mode

@@ -246,3 +246,23 @@ def test_long_rows_every_row(S, tile):
     fc.fc_causal_softmax(sd, out, SCALE, tile, fc.FC_SOFTMAX_FUSED)
     torch.cuda.synchronize()
     check_all_rows(s, 1, S, bf16_outs=[out])
+
+
+def random_softmax_shapes():
+    rng = np.random.default_rng(20261002 + 1)
+    return [(int(rng.integers(1, 4)), int(rng.integers(1, 1400))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("BH,S", random_softmax_shapes())
+def test_random_shapes_every_row(BH, S):
+    """Seeded random head counts and row lengths (most not a multiple of any
+    tile or of 8, so the generic kernel runs beside the vector one): the fused
+    form at every tile and the unfused baseline, every row against the oracle."""
+    announce(f"softmax random shape BH={BH} S={S}")
+    s = synth.softmax_inputs(BH, S, salt=BH * 7919 + S)
+    ref = oracle.causal_softmax_f64(s, SCALE)
+    sd = bf16_from_bits(s)
+    for tile in (64, 128, 256, S):
+        check_against_ref(run_fused(sd, BH, S, tile), ref, S)
+    out, _ = run_unfused(sd, BH, S)
+    check_against_ref(out, ref, S)
