@@ -383,3 +383,41 @@ def test_kernel_info_errors():
     assert fc.lib().fc_kernel_info(b"fc::attention_fwd_kernel", None, None, None, None, None, None) == fc.FC_OK
     assert fc.lib().fc_kernel_name(-1) is None
     assert fc.lib().fc_kernel_name(len(fc.fc_kernel_names())) is None
+
+
+def test_headers_compile_as_c_and_answer_from_c(tmp_path):
+    """A plain C99 program (tests/c_abi_check.c) built by gcc with -pedantic
+    -Werror against include/fc.h and include/fc_envelope.h, linked to the two
+    libraries: the declarations are C, and the host-only calls and argument
+    validation answer from C as they do through the binding."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    here = os.path.dirname(os.path.abspath(__file__))
+    libdir = os.path.dirname(fc.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.dirname(fc.HEADER), os.path.join(here, "c_abi_check.c"),
+                    "-L", libdir, "-lfc", "-lfcenv", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    assert got["version"] == fc.fc_version()
+    for name, plan in (("plan_bytes_4", [4]), ("plan_bytes_13", [1, 3]), ("plan_bytes_1111", [1, 1, 1, 1])):
+        assert int(got[name]) == ledger.plan_bytes(4096, 4096, 4096, plan)
+    assert int(got["plan_launches_1111"]) == 4
+    assert int(got["chain_bytes_fused"]) == ledger.chain_bytes(16777216, 8, True)
+    assert int(got["chain_bytes_naive"]) == ledger.chain_bytes(16777216, 8, False)
+    assert int(got["softmax_bytes_t64"]) == fc.fc_softmax_bytes(128, 2048, 64, fc.FC_SOFTMAX_FUSED)
+    assert int(got["workspace_13"]) == fc.fc_gemm_workspace_bytes(4096, 4096, 4096, [1, 3])
+    assert int(got["gemm_bad_plan"]) == fc.FC_ERR_PLAN
+    assert int(got["gemm_null"]) == fc.FC_ERR_NULL
+    assert int(got["noalloc_scratch"]) == fc.FC_ERR_SCRATCH
+    assert int(got["chain_k0"]) == fc.FC_ERR_UNSUPPORTED
+    assert int(got["softmax_bad_tile"]) == fc.FC_ERR_UNSUPPORTED
+    assert int(got["stages"]) == 0 and int(got["kernel_info"]) == 0
+    assert int(got["kernel_vgprs"]) == fc.fc_kernel_info("fc::attention_fwd_kernel")["vgprs"]
+    assert got["status_scratch"] == fc.fc_status_string(fc.FC_ERR_SCRATCH)
+    assert int(got["noalloc_limit"]) == fc.FC_GEMM_NOALLOC_SCRATCH_BYTES
+    assert int(got["envelope_bad"]) == fc.FC_ERR_NULL
