@@ -106,3 +106,39 @@ def test_noalloc_rejects_what_exceeds_its_scratch():
     torch.cuda.synchronize()
     ref = oracle.gemm_epilogue_f64_matmul(*h)
     assert within_bar(bits(Y), ref) <= 1.0
+
+
+def test_noalloc_captured_in_a_graph():
+    """The callers it is for: two calls (a split-K decode shape with a cut,
+    then a split-K 128x128-ring shape) captured in one HIP graph on torch's
+    capture stream and replayed four times, with eager work and synchronisation
+    between the replays: every replay gives the eager result bit for bit (the
+    arrival counters are cleared by a kernel, so the graph holds no memset)."""
+    announce("gemm noalloc captured in a graph")
+    calls = [((16, 4096, 4096), [1, 3], 970), ((200, 2048, 2048), [4], 971)]
+    data = []
+    for (M, N, K), plan, salt in calls:
+        h, d = make(M, N, K, salt)
+        data.append((h, d, plan, torch.empty((M, N), dtype=torch.float16, device="cuda")))
+
+    def work():
+        for _, d, plan, Y in data:
+            fc.fc_gemm_epilogue_noalloc(*d, Y, plan)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [bits(Y) for _, _, _, Y in data]
+    for (h, _, _, _), y in zip(data, eager):
+        assert within_bar(y, oracle.gemm_epilogue_f64_matmul(*h)) <= 1.0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for _, _, _, Y in data:
+            Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (_, _, _, Y) in enumerate(data):
+            assert np.array_equal(bits(Y), eager[i]), (rep, i)
