@@ -66,8 +66,9 @@ class Timer:
 
     A row is `reps` calls of the binding, launched from the host as they come
     (the host runs ahead of the GPU, so kernels follow each other without
-    gaps).  With graph=True the first run of a row captures its calls into a
-    HIP graph and from then on the row is one graph replay between the two
+    gaps).  With graph=True the first run of a row runs its calls once eagerly,
+    then captures them into a HIP graph, and from then on the row is one graph
+    replay between the two
     events; on this stack that adds one to two microseconds per kernel node, so
     it is not the default."""
 
@@ -83,6 +84,11 @@ class Timer:
         if not self.eager:
             g = self.graphs.get(name)
             if g is None:
+                # one eager run first: library handles (the vendor GEMM's among
+                # them) initialise outside the capture
+                for r in range(reps):
+                    fn(r)
+                t.cuda.synchronize()
                 g = t.cuda.CUDAGraph()
                 with t.cuda.graph(g):
                     for r in range(reps):
