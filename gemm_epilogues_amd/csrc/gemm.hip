@@ -767,7 +767,9 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
         // 16-byte unit u at u ^ ((u >> 4) & 1) ^ (r & 63): 16 lanes writing one
         // unit of 16 rows, or reading units 2c (or 2c + 1) of one row, cover all
         // 16 bank groups (no conflicts).  Same arithmetic per element as the
-        // accumulator-layout path.
+        // accumulator-layout path.  R and Y are touched once: streaming
+        // (nontemporal) loads and stores (4096 x 4096 x 512: 4 % faster,
+        // 1024..2048-row and K = 1024 shapes 1-2 %, 4096^3 unchanged).
         __syncthreads();                         // every wave is done with the ring
         FC_LDS float *sh = (FC_LDS float *)lds;
         const int rl = lane >> 5, cu = lane & 31;
@@ -787,7 +789,7 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 rw[q] = u32x4{0u, 0u, 0u, 0u};
-                if (LAST >= OP_RES) rw[q] = *reinterpret_cast<const u32x4 *>(R + rbase + (int64_t)q * 16 * N);
+                if (LAST >= OP_RES) rw[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(R + rbase + (int64_t)q * 16 * N));
             }
             if (wm == p) {
 #pragma unroll
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(ring::NT, 1) void gemm_ring_kernel(
                                      apply_ops<OP_BIAS, LAST>(x1.y, bv[5], f16_hi(rw[q].z)));
                 y.w = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x1.z, bv[6], f16_lo(rw[q].w)),
                                      apply_ops<OP_BIAS, LAST>(x1.w, bv[7], f16_hi(rw[q].w)));
-                *reinterpret_cast<u32x4 *>(out + rbase + (int64_t)q * 16 * N) = y;
+                __builtin_nontemporal_store(y, reinterpret_cast<u32x4 *>(out + rbase + (int64_t)q * 16 * N));
             }
             if (p == 0) __syncthreads();         // the next half overwrites what was just read
         }
@@ -1147,8 +1149,9 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
         // Interior tile: as the 256x256 kernel, the accumulators pass through
         // the freed ring (the whole 128x128 fp32 tile, 64 KiB, one pass) into a
         // row-major layout; a lane then finishes 8 consecutive columns of a
-        // row with 16-byte R loads and Y stores.  Row r at r * 512 bytes,
-        // 16-byte unit u at u ^ ((u >> 4) & 1) ^ (r & 31) (no bank conflicts).
+        // row with 16-byte R loads and Y stores (streaming, as in
+        // gemm_ring_kernel).  Row r at r * 512 bytes, 16-byte unit u at
+        // u ^ ((u >> 4) & 1) ^ (r & 31) (no bank conflicts).
         __syncthreads();                         // every wave is done with the ring
         FC_LDS float *sh = (FC_LDS float *)lds;
         const int rq = threadIdx.x >> 4, cu = threadIdx.x & 15;   // 16 rows x 16 lanes per pass of q
@@ -1165,7 +1168,7 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             rw[q] = u32x4{0u, 0u, 0u, 0u};
-            if (LAST >= OP_RES) rw[q] = *reinterpret_cast<const u32x4 *>(R + rbase + (int64_t)q * 16 * N);
+            if (LAST >= OP_RES) rw[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(R + rbase + (int64_t)q * 16 * N));
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -1194,7 +1197,7 @@ __global__ __launch_bounds__(r128::NT, 2) void gemm_ring128_kernel(
                                  apply_ops<OP_BIAS, LAST>(x1.y, bv[5], f16_hi(rw[q].z)));
             y.w = pack_f16x2_rne(apply_ops<OP_BIAS, LAST>(x1.z, bv[6], f16_lo(rw[q].w)),
                                  apply_ops<OP_BIAS, LAST>(x1.w, bv[7], f16_hi(rw[q].w)));
-            *reinterpret_cast<u32x4 *>(out + rbase + (int64_t)q * 16 * N) = y;
+            __builtin_nontemporal_store(y, reinterpret_cast<u32x4 *>(out + rbase + (int64_t)q * 16 * N));
         }
         return;
     }
