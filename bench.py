@@ -456,15 +456,22 @@ def measure_model_rows(torch, stream, groups, bufs, fc):
     out = {}
     sink = torch.zeros(64, dtype=torch.float32, device=dev)
     n_l = 200
-    ms = _median_ms(torch, stream, lambda r: env.fce_empty(256, sink), n_l, iters=9)
+    # per-kernel cost on the device's timeline: n_l empty kernels enqueued by
+    # one host call (as one library call enqueues the kernels of a split plan)
+    ms = _median_ms(torch, stream, lambda r: env.fce_empty_n(256, n_l, sink), 1, iters=9) / n_l
     out["launch_us"] = round(ms * 1e3, 3)
-    # t(n) for plain copies of n bytes (read n + write n), least-squares a + b * 2n
+    # the same kernel with one binding call per launch: the host's pace
+    ms = _median_ms(torch, stream, lambda r: env.fce_empty(256, sink), n_l, iters=9)
+    out["host_call_us"] = round(ms * 1e3, 3)
+    # t(n) for plain copies of n bytes (read n + write n), enqueued `reps` at a
+    # time by one host call; least-squares a + b * 2n
     big = torch.empty(2 * (256 << 20), dtype=torch.uint8, device=dev)
     src, dst = big[: 256 << 20], big[256 << 20:]
     pts = []
     for nb in (32 << 10, 256 << 10, 2 << 20, 16 << 20, 64 << 20, 256 << 20):
         reps = 50 if nb <= (2 << 20) else 10
-        t = _median_ms(torch, stream, lambda r, nb=nb: env.fce_mix(src, nb, dst, nb), reps, iters=7) * 1e-3
+        t = _median_ms(torch, stream, lambda r, nb=nb, reps=reps: env.fce_mix_n(src, nb, dst, nb, reps), 1,
+                       iters=7) * 1e-3 / reps
         pts.append((2 * nb, t))
     xs = [p[0] for p in pts]
     ys = [p[1] for p in pts]

@@ -125,19 +125,24 @@ __global__ void empty_kernel(float *__restrict__ sink)
 
 using namespace fce;
 
-extern "C" int fce_empty(int blocks, float *sink, fc_stream stream)
+extern "C" int fce_empty_n(int blocks, int n, float *sink, fc_stream stream)
 {
     if (!sink) return FC_ERR_NULL;
-    if (blocks < 1) return FC_ERR_SHAPE;
-    empty_kernel<<<blocks, 64, 0, reinterpret_cast<hipStream_t>(stream)>>>(sink);
+    if (blocks < 1 || n < 1) return FC_ERR_SHAPE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int k = 0; k < n; ++k) empty_kernel<<<blocks, 64, 0, s>>>(sink);
     return fc::launch_status();
 }
 
+extern "C" int fce_empty(int blocks, float *sink, fc_stream stream) { return fce_empty_n(blocks, 1, sink, stream); }
+
 extern "C" size_t fce_chunk_bytes(void) { return kChunk; }
 
-extern "C" int fce_mix(const void *src, size_t read_bytes, void *dst, size_t write_bytes, fc_stream stream)
+extern "C" int fce_mix_n(const void *src, size_t read_bytes, void *dst, size_t write_bytes, int n,
+                         fc_stream stream)
 {
     if (!dst || (read_bytes && !src)) return FC_ERR_NULL;
+    if (n < 1) return FC_ERR_SHAPE;
     if (write_bytes == 0 || write_bytes % kChunk || read_bytes % kChunk || read_bytes > write_bytes)
         return FC_ERR_SHAPE;
     if (!fc::aligned16(src) || !fc::aligned16(dst)) return FC_ERR_ALIGN;
@@ -147,13 +152,20 @@ extern "C" int fce_mix(const void *src, size_t read_bytes, void *dst, size_t wri
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const f32x4 *in = static_cast<const f32x4 *>(src);
     f32x4 *out = static_cast<f32x4 *>(dst);
-    if (rc == wc)
-        mix_kernel<0><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
-    else if (rc == 0)
-        mix_kernel<1><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
-    else
-        mix_kernel<2><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
+    for (int k = 0; k < n; ++k) {
+        if (rc == wc)
+            mix_kernel<0><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
+        else if (rc == 0)
+            mix_kernel<1><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
+        else
+            mix_kernel<2><<<(unsigned)wc, kBlock, 0, s>>>(in, out, rc, wc);
+    }
     return fc::launch_status();
+}
+
+extern "C" int fce_mix(const void *src, size_t read_bytes, void *dst, size_t write_bytes, fc_stream stream)
+{
+    return fce_mix_n(src, read_bytes, dst, write_bytes, 1, stream);
 }
 
 // Flat granule: 256 lanes x 16 bytes.

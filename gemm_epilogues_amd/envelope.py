@@ -27,9 +27,11 @@ _lib.fce_mfma.restype, _lib.fce_mfma.argtypes = _I, [_P, _I, _P]
 _lib.fce_mfma_sink_floats.restype, _lib.fce_mfma_sink_floats.argtypes = _SZ, []
 _lib.fce_mfma_flops.restype, _lib.fce_mfma_flops.argtypes = ctypes.c_double, [_I]
 _lib.fce_empty.restype, _lib.fce_empty.argtypes = _I, [_I, _P, _P]
+_lib.fce_empty_n.restype, _lib.fce_empty_n.argtypes = _I, [_I, _I, _P, _P]
+_lib.fce_mix_n.restype, _lib.fce_mix_n.argtypes = _I, [_P, _SZ, _P, _SZ, _I, _P]
 
 EXPORTED = ("fce_chunk_bytes", "fce_mix", "fce_read", "fce_flat", "fce_mfma", "fce_mfma_sink_floats",
-            "fce_mfma_flops", "fce_empty")
+            "fce_mfma_flops", "fce_empty", "fce_empty_n", "fce_mix_n")
 
 
 def _addr(t):
@@ -77,3 +79,14 @@ def fce_mfma(sink, iters: int, stream=None) -> None:
 
 def fce_empty(blocks: int, sink, stream=None) -> None:
     fc._check(_lib.fce_empty(int(blocks), _addr(sink), _stream(stream)), "fce_empty")
+
+
+def fce_empty_n(blocks: int, n: int, sink, stream=None) -> None:
+    """n empty kernels back to back from one call."""
+    fc._check(_lib.fce_empty_n(int(blocks), int(n), _addr(sink), _stream(stream)), "fce_empty_n")
+
+
+def fce_mix_n(src, read_bytes: int, dst, write_bytes: int, n: int, stream=None) -> None:
+    """fce_mix n times back to back from one call."""
+    fc._check(_lib.fce_mix_n(_addr(src), int(read_bytes), _addr(dst), int(write_bytes), int(n), _stream(stream)),
+              "fce_mix_n")

@@ -36,6 +36,11 @@ size_t fce_chunk_bytes(void);
  */
 int fce_mix(const void *src, size_t read_bytes, void *dst, size_t write_bytes, fc_stream stream);
 
+/* fce_mix_n -- fce_mix launched n >= 1 times back to back from this one call
+ * (n < 1: FC_ERR_SHAPE), so that a stream of small copies is timed without a
+ * host call per kernel. */
+int fce_mix_n(const void *src, size_t read_bytes, void *dst, size_t write_bytes, int n, fc_stream stream);
+
 /*
  * fce_flat -- a flat stream of `bytes` (a multiple of 4 KiB) in the shape
  * with the smallest workgroup footprint: one 16-byte vector per lane, one
@@ -65,6 +70,12 @@ double fce_mfma_flops(int iters);
  * float never written): back-to-back launches of it time the per-kernel
  * overhead of a stream. */
 int fce_empty(int blocks, float *sink, fc_stream stream);
+
+/* fce_empty_n -- n >= 1 such kernels launched back to back from this one call:
+ * their time over n is the per-kernel cost on the device's timeline when the
+ * host is not the bottleneck (as for the kernels of one split plan, which one
+ * library call enqueues).  FC_ERR_NULL (sink), FC_ERR_SHAPE (blocks or n < 1). */
+int fce_empty_n(int blocks, int n, float *sink, fc_stream stream);
 
 #ifdef __cplusplus
 }

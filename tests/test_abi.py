@@ -279,6 +279,10 @@ def test_envelope_validation_before_launch():
     assert L.fce_mfma(FAKE, 0, None) == fc.FC_ERR_SHAPE
     assert L.fce_empty(0, FAKE, None) == fc.FC_ERR_SHAPE
     assert L.fce_empty(4, None, None) == fc.FC_ERR_NULL
+    assert L.fce_empty_n(4, 0, FAKE, None) == fc.FC_ERR_SHAPE
+    assert L.fce_empty_n(4, 3, None, None) == fc.FC_ERR_NULL
+    assert L.fce_mix_n(FAKE, C, FAKE + 4 * C, C, 0, None) == fc.FC_ERR_SHAPE
+    assert L.fce_mix_n(FAKE, C, FAKE + C // 2, C, 2, None) == fc.FC_ERR_ALIAS
 
 
 def test_attention_accounting_and_validation():

@@ -77,3 +77,25 @@ def test_flat_streams():
     lane = np.arange(d.shape[0]) % 256
     assert np.array_equal(d, np.stack([np.full(lane.size, 1.0), np.full(lane.size, 2.0), np.full(lane.size, 3.0),
                                        lane.astype(np.float64)], 1).astype(np.float32))
+
+
+def test_repeated_launch_probes():
+    """fce_mix_n and fce_empty_n launch their kernel n times: a copy repeated
+    three times leaves the plain copy, and a mixed stream the same bytes as
+    one call."""
+    announce("envelope repeated launches")
+    dev = torch.device("cuda", 0)
+    wc, rc = 24, 7
+    src = torch.randint(-2**31, 2**31 - 1, (wc * C // 4,), dtype=torch.int32, device=dev)
+    dst, dst1 = torch.zeros_like(src), torch.zeros_like(src)
+    env.fce_mix_n(src, wc * C, dst, wc * C, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    env.fce_mix(src, rc * C, dst1, wc * C)
+    env.fce_mix_n(src, rc * C, dst, wc * C, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, dst1)
+    sink = torch.full((1,), 3.0, device=dev)
+    env.fce_empty_n(256, 50, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 3.0
